@@ -1,0 +1,122 @@
+/*
+ * ssw.h -- C ABI of libssw.so: Stochastic Attention (SA), sliding-window attention (SWA) and the
+ * gated SA+SWA forward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (from the pages):
+ *   [SA-ja] "技術的概要：確率的アテンション" (gist.science/ja/paper/2604.00754), 手法 › 中核メカニズム:
+ *     1. Permute: draw sigma ~ Uniform(S_n) for each layer, reorder the Q, K, V token rows by it;
+ *     2. window attention: run standard sliding-window attention of window w in the permuted
+ *        space (理論的性質 › 因果的制約: in the autoregressive setting the causal mask keeps only
+ *        tokens that precede the query in the original order);
+ *     3. Undo permute: apply sigma^-1 to the output.
+ *   ゲート付き SA と SWA の組み合わせ: Y = g_sa (.) Y_sa + g_swa (.) Y_swa.
+ *   [HYB] notes on "Rethinking the Role of Efficient Attention in Hybrid Architectures",
+ *     ハイブリッドアーキテクチャの定義: SWA restricts position t to the w tokens before it.
+ *
+ * Exact semantics implemented (the readings of what the pages leave open):
+ *   sigma[p] is the ORIGINAL index of the token at permuted slot p (gather convention).
+ *   Query at slot p sees the keys at slots q with |p - q| <= w - 1, truncated at 0 and n - 1;
+ *   when causal, only those with sigma[q] <= sigma[p].  With sigma = identity this is causal SWA
+ *   over [t - w + 1, t].  Scores are scaled by 1/sqrt(d).  Query head h reads KV head
+ *   h / (Hq / Hkv).  The output row of slot p is written at original position sigma[p].
+ *
+ * Layouts (all row-major, contiguous, token-major "BSHD"):
+ *   q, out  [B, n, Hq,  d]     k, v  [B, n, Hkv, d]     element type given by `dtype`
+ *   sigma   int32 [n]          one permutation per call, shared by every batch row and head
+ *   gate    float32 [B, n, Hq] (single-path calls, optional)
+ *   gates   float32 [2, B, n, Hq] (gated call; g_sa first, then g_swa), indexed by ORIGINAL
+ *           token position, broadcast over d.
+ *
+ * Ownership and execution: every tensor pointer of the forward calls is a DEVICE pointer owned
+ * by the caller; the library never allocates, frees or keeps them.  Work is enqueued on
+ * `stream` (a hipStream_t; NULL = the default stream) and the call returns without waiting.
+ * q, k, v and out must not overlap.  Inputs are not modified.
+ *
+ * Errors: every entry point returns SSW_OK (0) or a negative ssw_status and never aborts or
+ * throws.  Arguments are checked before anything is enqueued; on an error nothing is launched
+ * and ssw_last_error() (per calling thread) describes it.  B == 0 or n == 0 is a valid empty
+ * call that does nothing.
+ */
+#ifndef SSW_H
+#define SSW_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSW_F32 = 0, SSW_BF16 = 1 } ssw_dtype;
+
+typedef enum {
+  SSW_OK = 0,
+  SSW_EINVAL = -1,   /* window < 1, negative size, NULL required pointer, causal not 0/1 */
+  SSW_ESHAPE = -2,   /* Hq not a multiple of Hkv, or sizes whose index range overflows */
+  SSW_EDTYPE = -3,   /* d not 64 or 128, or dtype not SSW_F32 / SSW_BF16 */
+  SSW_EALIGN = -4,   /* q, k, v, out not 16-byte aligned; sigma, gates not 4-byte aligned */
+  SSW_ENOTPERM = -5, /* sigma is not a permutation of [0, n) (only detected when checked) */
+  SSW_EHIP = -6      /* a HIP runtime call or kernel launch failed */
+} ssw_status;
+
+/* Stochastic Attention forward ([SA-ja] 中核メカニズム steps 1-3, 因果的制約).
+ *   q, k, v   device, layouts above, element type `dtype`.
+ *   sigma     device int32[n], a permutation of [0, n).  It is trusted; set the environment
+ *             variable SSW_VALIDATE=1 to have every call copy it back and check it (slow,
+ *             synchronous; returns SSW_ENOTPERM on failure).
+ *   window    w >= 1 (values >= n behave as n: full attention, causal or not).
+ *   causal    0 or 1.
+ *   gate      device float32 [B, n, Hq] or NULL: out = gate (.) Y_sa when given, else Y_sa.
+ *   out       device, [B, n, Hq, d], type `dtype`; fully overwritten.
+ *   d         64 or 128.  dtype SSW_F32 or SSW_BF16 (fp32 accumulation either way; bf16
+ *             results are rounded to nearest even once, at the store). */
+int ssw_sa_forward(const void* q, const void* k, const void* v, const int32_t* sigma,
+                   int window, int causal, const float* gate, void* out,
+                   int B, int n, int Hq, int Hkv, int d, int dtype, void* stream);
+
+/* Sliding-window attention forward ([HYB] ハイブリッドアーキテクチャの定義): the same operator
+ * with sigma = identity.  `sigma` must be NULL (anything else is SSW_EINVAL).  Other arguments
+ * as in ssw_sa_forward. */
+int ssw_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma,
+                    int window, int causal, const float* gate, void* out,
+                    int B, int n, int Hq, int Hkv, int d, int dtype, void* stream);
+
+/* Gated dual path ([SA-ja] ゲート付き SA と SWA の組み合わせ):
+ *   out = g_sa (.) SA(q, k, v; sigma, w, causal) + g_swa (.) SWA(q, k, v; w, causal).
+ *   gates     device float32 [2, B, n, Hq], required.  Both paths use the same w and causal.
+ * Two kernels run back to back on `stream`: the SA pass stores g_sa (.) Y_sa into `out`, then
+ * the SWA pass reads it, adds g_swa (.) Y_swa and stores the sum.  In bf16 the SA partial is
+ * rounded to bf16 once before the final rounding.  Other arguments as in ssw_sa_forward. */
+int ssw_gated_sa_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma,
+                             int window, int causal, const float* gates, void* out,
+                             int B, int n, int Hq, int Hkv, int d, int dtype, void* stream);
+
+/* Host helpers (HOST pointers, no GPU needed). */
+
+/* sigma ~ Uniform(S_n) for one layer ([SA-ja] 中核メカニズム step 1) from a seeded Fisher-Yates
+ * shuffle (Durstenfeld form, i from n-1 down to 1, j = floor(r * (i + 1) / 2^64)) driven by
+ * splitmix64 (Steele, Lea & Flood 2014; state starts at `seed`).  Writes sigma_out[n] and, when
+ * inv_out is not NULL, inv_out[n] with inv_out[sigma_out[p]] = p.  n >= 0. */
+int ssw_make_permutation(uint64_t seed, int n, int32_t* sigma_out, int32_t* inv_out);
+
+/* inv_out[sigma[p]] = p (the un-permute map of [SA-ja] step 3); SSW_ENOTPERM if sigma is not a
+ * permutation of [0, n). */
+int ssw_inverse_permutation(const int32_t* sigma, int n, int32_t* inv_out);
+
+/* SSW_OK if sigma (host) is a permutation of [0, n), else SSW_ENOTPERM. */
+int ssw_check_permutation(const int32_t* sigma, int n);
+
+/* Debug: neighbour sets as a bitmask, computed on the device with the same membership test the
+ * attention kernels use.  bits (device uint32 [n][ceil(n/32)], fully overwritten): bit j of row i
+ * is set iff original token i attends to original token j.  sigma (device int32[n]) or NULL for
+ * SWA.  Meant for small n (n <= 4096). */
+int ssw_neighbor_mask(const int32_t* sigma, int n, int window, int causal, uint32_t* bits,
+                      void* stream);
+
+/* Message describing the most recent failed call on the calling thread ("" if none). */
+const char* ssw_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSW_H */

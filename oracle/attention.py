@@ -37,6 +37,22 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
+def _exact(x) -> np.ndarray:
+    """A NumPy view holding exactly the values of x, without widening to float64 yet.
+
+    bfloat16 and float32 tensors become float32 arrays (every bfloat16 value is a float32 value),
+    float64 stays float64.  Rows are widened to float64 where they enter arithmetic, so large
+    inputs need not be copied whole.
+    """
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        x = x.numpy() if str(x.dtype) in ("torch.float32", "torch.float64") else x.float().numpy()
+    x = np.asarray(x)
+    if x.dtype not in (np.float32, np.float64):
+        x = x.astype(np.float64)
+    return x
+
+
 # ----------------------------------------------------------------------------------------------
 # Neighbour sets
 # ----------------------------------------------------------------------------------------------
@@ -88,11 +104,12 @@ def _attend_row(q_i: np.ndarray, k_b: np.ndarray, v_b: np.ndarray, idx: np.ndarr
     q_i [Hq, d]; k_b, v_b [n, Hkv, d]; idx int[m].  Returns [Hq, d].  The softmax subtracts
     the row maximum before exponentiating (the value is unchanged by it).
     """
+    q_i = q_i.astype(np.float64)
     hq, d = q_i.shape
     hkv = k_b.shape[1]
     g = hq // hkv
-    kj = k_b[idx]                                   # [m, Hkv, d]
-    vj = v_b[idx]                                   # [m, Hkv, d]
+    kj = k_b[idx].astype(np.float64)                # [m, Hkv, d]
+    vj = v_b[idx].astype(np.float64)                # [m, Hkv, d]
     out = np.empty((hq, d), dtype=np.float64)
     for h in range(hq):
         kvh = h // g                                # R7
@@ -125,7 +142,7 @@ def sa_rows(q, k, v, sigma, window: int, causal: bool,
     [SA-ja] 中核メカニズム steps 1-3 + 理論的性質 (因果的制約), evaluated in original token space:
     Y_sa[i] = sum over j in N~^sigma_w(i) of softmax_j(<Q_i, K_j>/sqrt(d)) V_j   (R5).
     """
-    q, k, v = _f64(q), _f64(k), _f64(v)
+    q, k, v = _exact(q), _exact(k), _exact(v)
     b_, n, hq, d = _check_shapes(q, k, v)
     if window < 1:
         raise ValueError("window must be >= 1")
@@ -146,7 +163,7 @@ def sa_rows(q, k, v, sigma, window: int, causal: bool,
 def swa_rows(q, k, v, window: int, causal: bool,
              rows: Optional[Iterable[int]] = None) -> np.ndarray:
     """Y_swa at the given original token indices: plain sliding-window attention ([HYB], R2)."""
-    q, k, v = _f64(q), _f64(k), _f64(v)
+    q, k, v = _exact(q), _exact(k), _exact(v)
     b_, n, hq, d = _check_shapes(q, k, v)
     if window < 1:
         raise ValueError("window must be >= 1")

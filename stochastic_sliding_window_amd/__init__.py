@@ -1,0 +1,238 @@
+"""Stochastic Attention (SA), SWA and gated SA+SWA forward for AMD MI355X (gfx950).
+
+Thin ctypes binding over the C ABI of ``libssw.so`` (declared in ``include/ssw.h``).  Every
+function here only marshals arguments -- tensor checks, device pointers, the current HIP stream
+-- and calls the library; all arithmetic runs in the library's HIP kernels (or, for the
+permutation helpers, its host C++ code).  PyTorch supplies device memory and streams.
+
+The functions keep the C names without the ``ssw_`` prefix:
+
+    sa_forward(q, k, v, sigma, window, causal, gate=None, out=None)
+    swa_forward(q, k, v, window, causal, gate=None, out=None)
+    gated_sa_swa_forward(q, k, v, sigma, window, causal, gates, out=None)
+    make_permutation(seed, n) / inverse_permutation(sigma) / check_permutation(sigma)
+    neighbor_mask(sigma, n, window, causal)
+
+There is no fallback: if ``libssw.so`` has not been built, importing this package raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "SSWError", "LIB_PATH", "sa_forward", "swa_forward", "gated_sa_swa_forward",
+    "make_permutation", "inverse_permutation", "check_permutation", "neighbor_mask",
+    "last_error", "F32", "BF16",
+]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libssw.so")
+
+F32 = 0
+BF16 = 1
+
+_STATUS = {
+    0: "SSW_OK", -1: "SSW_EINVAL", -2: "SSW_ESHAPE", -3: "SSW_EDTYPE", -4: "SSW_EALIGN",
+    -5: "SSW_ENOTPERM", -6: "SSW_EHIP",
+}
+
+
+class SSWError(RuntimeError):
+    """A libssw call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first with "
+            "`python -m stochastic_sliding_window_amd.build` (needs ROCm hipcc)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32p, i32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+    fwd = [vp, vp, vp, i32p, i32, i32, f32p, vp, i32, i32, i32, i32, i32, i32, vp]
+    for name in ("ssw_sa_forward", "ssw_swa_forward", "ssw_gated_sa_swa_forward"):
+        fn = getattr(lib, name)
+        fn.argtypes = fwd
+        fn.restype = ctypes.c_int
+    lib.ssw_make_permutation.argtypes = [ctypes.c_uint64, i32, i32p, i32p]
+    lib.ssw_make_permutation.restype = ctypes.c_int
+    lib.ssw_inverse_permutation.argtypes = [i32p, i32, i32p]
+    lib.ssw_inverse_permutation.restype = ctypes.c_int
+    lib.ssw_check_permutation.argtypes = [i32p, i32]
+    lib.ssw_check_permutation.restype = ctypes.c_int
+    lib.ssw_neighbor_mask.argtypes = [i32p, i32, i32, i32, vp, vp]
+    lib.ssw_neighbor_mask.restype = ctypes.c_int
+    lib.ssw_last_error.argtypes = []
+    lib.ssw_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def last_error() -> str:
+    return _lib.ssw_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise SSWError(status, last_error())
+
+
+# ------------------------------------------------------------------------------------------
+# host helpers
+# ------------------------------------------------------------------------------------------
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def make_permutation(seed: int, n: int, with_inverse: bool = False):
+    """sigma (int32[n]) for one layer from the seeded generator; optionally also sigma^-1."""
+    sigma = np.empty(n, dtype=np.int32)
+    inv = np.empty(n, dtype=np.int32) if with_inverse else None
+    _check(_lib.ssw_make_permutation(ctypes.c_uint64(seed & (2**64 - 1)), n, _np_ptr(sigma),
+                                     _np_ptr(inv) if inv is not None else None))
+    return (sigma, inv) if with_inverse else sigma
+
+
+def inverse_permutation(sigma) -> np.ndarray:
+    s = np.ascontiguousarray(np.asarray(sigma, dtype=np.int32))
+    inv = np.empty_like(s)
+    _check(_lib.ssw_inverse_permutation(_np_ptr(s), s.shape[0], _np_ptr(inv)))
+    return inv
+
+
+def check_permutation(sigma) -> bool:
+    s = np.ascontiguousarray(np.asarray(sigma, dtype=np.int32))
+    st = _lib.ssw_check_permutation(_np_ptr(s), s.shape[0])
+    if st == -5:
+        return False
+    _check(st)
+    return True
+
+
+# ------------------------------------------------------------------------------------------
+# device entry points
+# ------------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream_handle(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev_ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _prep(q, k, v, out):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a device tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, n, H, d] tensor")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("k and v must be [B, n, Hkv, d] matching q [B, n, Hq, d]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous device tensor shaped and typed like q")
+    return out
+
+
+def _prep_sigma(sigma, n, device):
+    torch = _torch()
+    if not isinstance(sigma, torch.Tensor) or sigma.dtype != torch.int32 or \
+            sigma.shape != (n,) or not sigma.is_contiguous() or sigma.device != device:
+        raise ValueError("sigma must be a contiguous int32 [n] tensor on the same device as q")
+    return sigma
+
+
+def _prep_gate(gate, shape, device):
+    torch = _torch()
+    if gate is None:
+        return None
+    if gate.dtype != torch.float32 or tuple(gate.shape) != tuple(shape) or \
+            not gate.is_contiguous() or gate.device != device:
+        raise ValueError(f"gate must be a contiguous float32 {tuple(shape)} tensor on q's device")
+    return gate
+
+
+def sa_forward(q, k, v, sigma, window: int, causal: bool, gate=None, out=None):
+    """Stochastic Attention forward: out[b, sigma[p], h] = SWA_w in permuted space (ssw_sa_forward)."""
+    out = _prep(q, k, v, out)
+    B, n, Hq, d = q.shape
+    sigma = _prep_sigma(sigma, n, q.device)
+    gate = _prep_gate(gate, (B, n, Hq), q.device)
+    _check(_lib.ssw_sa_forward(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sigma), int(window),
+                               int(bool(causal)), _dev_ptr(gate), _dev_ptr(out), B, n, Hq,
+                               k.shape[2], d, _dtype_code(q), _stream_handle(q)))
+    return out
+
+
+def swa_forward(q, k, v, window: int, causal: bool, gate=None, out=None):
+    """Plain sliding-window attention forward (ssw_swa_forward)."""
+    out = _prep(q, k, v, out)
+    B, n, Hq, d = q.shape
+    gate = _prep_gate(gate, (B, n, Hq), q.device)
+    _check(_lib.ssw_swa_forward(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), None, int(window),
+                                int(bool(causal)), _dev_ptr(gate), _dev_ptr(out), B, n, Hq,
+                                k.shape[2], d, _dtype_code(q), _stream_handle(q)))
+    return out
+
+
+def gated_sa_swa_forward(q, k, v, sigma, window: int, causal: bool, gates, out=None):
+    """Y = g_sa * SA + g_swa * SWA with gates [2, B, n, Hq] (ssw_gated_sa_swa_forward)."""
+    out = _prep(q, k, v, out)
+    B, n, Hq, d = q.shape
+    sigma = _prep_sigma(sigma, n, q.device)
+    if gates is None:
+        raise ValueError("gates are required")
+    gates = _prep_gate(gates, (2, B, n, Hq), q.device)
+    _check(_lib.ssw_gated_sa_swa_forward(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sigma),
+                                         int(window), int(bool(causal)), _dev_ptr(gates),
+                                         _dev_ptr(out), B, n, Hq, k.shape[2], d, _dtype_code(q),
+                                         _stream_handle(q)))
+    return out
+
+
+def neighbor_mask(sigma, n: int, window: int, causal: bool, device=None):
+    """uint32 [n, ceil(n/32)] device bitmask of the neighbour sets (ssw_neighbor_mask).
+
+    sigma: int32 [n] device tensor, or None for SWA.
+    """
+    torch = _torch()
+    if sigma is not None:
+        device = sigma.device
+        sigma = _prep_sigma(sigma, n, device)
+    words = (n + 31) // 32
+    bits = torch.empty((n, words), dtype=torch.int32, device=device)
+    _check(_lib.ssw_neighbor_mask(_dev_ptr(sigma), n, int(window), int(bool(causal)),
+                                  _dev_ptr(bits), ctypes.c_void_p(
+                                      torch.cuda.current_stream(bits.device).cuda_stream)))
+    return bits

@@ -1,0 +1,34 @@
+// Internal interface between the C-ABI host code (ssw_api.cpp) and the gfx950 kernels
+// (band_attn.hip).  Not installed; the public interface is include/ssw.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace ssw {
+
+// One band-attention launch.  `perm` selects the stochastic (sigma-gathered) operator; without
+// it sigma is the identity (plain SWA).  `accumulate` adds gate * Y to the existing contents of
+// `out` instead of overwriting it (second pass of the gated path).
+struct BandLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* sigma;  // device int32[n] when perm, else ignored
+  const float* gate;     // device float32 [B, n, Hq] or nullptr
+  void* out;
+  int B, n, Hq, Hkv, d;
+  int dtype;             // 0 = fp32, 1 = bf16
+  int window;            // already clamped to [1, n]
+  bool causal;
+  bool perm;
+  bool accumulate;
+};
+
+hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream);
+
+// bits [n][ceil(n/32)] uint32, overwritten.  sigma may be nullptr (identity).
+hipError_t launch_neighbor_mask(const int32_t* sigma, int n, int window, bool causal,
+                                uint32_t* bits, hipStream_t stream);
+
+}  // namespace ssw

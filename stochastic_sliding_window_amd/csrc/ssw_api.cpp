@@ -1,0 +1,230 @@
+// C ABI of libssw.so (declared in include/ssw.h): argument checking, the host-side permutation
+// generator and dispatch of the gfx950 kernels in band_attn.hip.
+//
+// Nothing here allocates device memory; forward calls only enqueue kernels on the caller's
+// stream.  Errors are reported as negative status codes plus a per-thread message; no C++
+// exception crosses the ABI.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/ssw.h"
+#include "band_attn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// splitmix64 (Steele, Lea & Flood 2014): advance the state by the golden-ratio increment, then
+// finalise it with two xor-shift/multiply rounds and a last xor-shift.
+struct SplitMix64 {
+  uint64_t state;
+  uint64_t next() {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }
+};
+
+// Shared checks of the three forward entry points.
+int check_forward(const char* who, const void* q, const void* k, const void* v, const void* out,
+                  int window, int causal, int B, int n, int Hq, int Hkv, int d, int dtype) {
+  const std::string w(who);
+  if (B < 0 || n < 0) return fail(SSW_EINVAL, w + ": B and n must be >= 0");
+  if (window < 1) return fail(SSW_EINVAL, w + ": window must be >= 1");
+  if (causal != 0 && causal != 1) return fail(SSW_EINVAL, w + ": causal must be 0 or 1");
+  if (Hq < 1 || Hkv < 1) return fail(SSW_EINVAL, w + ": Hq and Hkv must be >= 1");
+  if (Hq % Hkv != 0) return fail(SSW_ESHAPE, w + ": Hq must be a multiple of Hkv");
+  if (dtype != SSW_F32 && dtype != SSW_BF16) return fail(SSW_EDTYPE, w + ": unsupported dtype");
+  if (d != 64 && d != 128) return fail(SSW_EDTYPE, w + ": head dim d must be 64 or 128");
+  // every index the kernels form must stay inside int32 where they use int32
+  const int64_t G = Hq / Hkv;
+  if ((int64_t)n * G > ((int64_t)1 << 31) - 4096 || (int64_t)B * Hkv >= 65536)
+    return fail(SSW_ESHAPE, w + ": n * Hq / Hkv must be <= 2^31 - 4096 and B * Hkv < 65536");
+  if (B == 0 || n == 0) return SSW_OK;
+  if (!q || !k || !v || !out) return fail(SSW_EINVAL, w + ": q, k, v and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(SSW_EALIGN, w + ": q, k, v and out must be 16-byte aligned");
+  return SSW_OK;
+}
+
+int check_sigma_on_device(const int32_t* sigma, int n, hipStream_t stream) {
+  std::vector<int32_t> host((size_t)n);
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess)
+    e = hipMemcpy(host.data(), sigma, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess)
+    return fail(SSW_EHIP, std::string("SSW_VALIDATE copy of sigma failed: ") + hipGetErrorString(e));
+  if (ssw_check_permutation(host.data(), n) != SSW_OK)
+    return fail(SSW_ENOTPERM, "sigma is not a permutation of [0, n)");
+  return SSW_OK;
+}
+
+bool validate_requested() {
+  const char* s = getenv("SSW_VALIDATE");
+  return s && s[0] == '1';
+}
+
+int run(const char* who, const ssw::BandLaunch& a, hipStream_t stream) {
+  hipError_t e = ssw::launch_band_attn(a, stream);
+  if (e != hipSuccess)
+    return fail(SSW_EHIP, std::string(who) + ": kernel launch failed: " + hipGetErrorString(e));
+  return SSW_OK;
+}
+
+ssw::BandLaunch make_launch(const void* q, const void* k, const void* v, const int32_t* sigma,
+                            int window, int causal, const float* gate, void* out, int B, int n,
+                            int Hq, int Hkv, int d, int dtype) {
+  ssw::BandLaunch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.sigma = sigma;
+  a.gate = gate;
+  a.out = out;
+  a.B = B;
+  a.n = n;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.dtype = dtype;
+  a.window = window < n ? window : n;  // a band of n - 1 already covers every slot
+  a.causal = causal != 0;
+  a.perm = sigma != nullptr;
+  a.accumulate = false;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssw_sa_forward(const void* q, const void* k, const void* v, const int32_t* sigma, int window,
+                   int causal, const float* gate, void* out, int B, int n, int Hq, int Hkv, int d,
+                   int dtype, void* stream) {
+  int st = check_forward("ssw_sa_forward", q, k, v, out, window, causal, B, n, Hq, Hkv, d, dtype);
+  if (st != SSW_OK || B == 0 || n == 0) return st;
+  if (!sigma) return fail(SSW_EINVAL, "ssw_sa_forward: sigma must be non-NULL");
+  if (!aligned(sigma, 4) || (gate && !aligned(gate, 4)))
+    return fail(SSW_EALIGN, "ssw_sa_forward: sigma and gate must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_requested()) {
+    st = check_sigma_on_device(sigma, n, s);
+    if (st != SSW_OK) return st;
+  }
+  return run("ssw_sa_forward",
+             make_launch(q, k, v, sigma, window, causal, gate, out, B, n, Hq, Hkv, d, dtype), s);
+}
+
+int ssw_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma, int window,
+                    int causal, const float* gate, void* out, int B, int n, int Hq, int Hkv, int d,
+                    int dtype, void* stream) {
+  int st = check_forward("ssw_swa_forward", q, k, v, out, window, causal, B, n, Hq, Hkv, d, dtype);
+  if (st != SSW_OK || B == 0 || n == 0) return st;
+  if (sigma) return fail(SSW_EINVAL, "ssw_swa_forward: sigma must be NULL (identity)");
+  if (gate && !aligned(gate, 4)) return fail(SSW_EALIGN, "ssw_swa_forward: gate must be 4-byte aligned");
+  return run("ssw_swa_forward",
+             make_launch(q, k, v, nullptr, window, causal, gate, out, B, n, Hq, Hkv, d, dtype),
+             (hipStream_t)stream);
+}
+
+int ssw_gated_sa_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma,
+                             int window, int causal, const float* gates, void* out, int B, int n,
+                             int Hq, int Hkv, int d, int dtype, void* stream) {
+  int st = check_forward("ssw_gated_sa_swa_forward", q, k, v, out, window, causal, B, n, Hq, Hkv,
+                         d, dtype);
+  if (st != SSW_OK || B == 0 || n == 0) return st;
+  if (!sigma || !gates)
+    return fail(SSW_EINVAL, "ssw_gated_sa_swa_forward: sigma and gates must be non-NULL");
+  if (!aligned(sigma, 4) || !aligned(gates, 4))
+    return fail(SSW_EALIGN, "ssw_gated_sa_swa_forward: sigma and gates must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_requested()) {
+    st = check_sigma_on_device(sigma, n, s);
+    if (st != SSW_OK) return st;
+  }
+  const float* g_sa = gates;
+  const float* g_swa = gates + (size_t)B * n * Hq;
+  // pass 1: out = g_sa * Y_sa (scattered through sigma)
+  st = run("ssw_gated_sa_swa_forward",
+           make_launch(q, k, v, sigma, window, causal, g_sa, out, B, n, Hq, Hkv, d, dtype), s);
+  if (st != SSW_OK) return st;
+  // pass 2: out += g_swa * Y_swa (stream order makes the read-modify-write race-free)
+  ssw::BandLaunch a2 =
+      make_launch(q, k, v, nullptr, window, causal, g_swa, out, B, n, Hq, Hkv, d, dtype);
+  a2.accumulate = true;
+  return run("ssw_gated_sa_swa_forward", a2, s);
+}
+
+int ssw_make_permutation(uint64_t seed, int n, int32_t* sigma_out, int32_t* inv_out) {
+  if (n < 0) return fail(SSW_EINVAL, "ssw_make_permutation: n must be >= 0");
+  if (n > 0 && !sigma_out) return fail(SSW_EINVAL, "ssw_make_permutation: sigma_out is NULL");
+  for (int i = 0; i < n; ++i) sigma_out[i] = i;
+  SplitMix64 rng{seed};
+  for (int i = n - 1; i >= 1; --i) {
+    // Lemire's multiply-high map of a 64-bit draw onto [0, i]
+    const unsigned __int128 prod = (unsigned __int128)rng.next() * (unsigned __int128)(i + 1);
+    const int j = (int)(uint64_t)(prod >> 64);
+    const int32_t t = sigma_out[i];
+    sigma_out[i] = sigma_out[j];
+    sigma_out[j] = t;
+  }
+  if (inv_out)
+    for (int p = 0; p < n; ++p) inv_out[sigma_out[p]] = p;
+  return SSW_OK;
+}
+
+int ssw_check_permutation(const int32_t* sigma, int n) {
+  if (n < 0) return fail(SSW_EINVAL, "ssw_check_permutation: n must be >= 0");
+  if (n == 0) return SSW_OK;
+  if (!sigma) return fail(SSW_EINVAL, "ssw_check_permutation: sigma is NULL");
+  std::vector<uint8_t> seen((size_t)n, 0);
+  for (int p = 0; p < n; ++p) {
+    const int32_t s = sigma[p];
+    if (s < 0 || s >= n || seen[(size_t)s])
+      return fail(SSW_ENOTPERM, "sigma is not a permutation of [0, n)");
+    seen[(size_t)s] = 1;
+  }
+  return SSW_OK;
+}
+
+int ssw_inverse_permutation(const int32_t* sigma, int n, int32_t* inv_out) {
+  const int st = ssw_check_permutation(sigma, n);
+  if (st != SSW_OK) return st;
+  if (n > 0 && !inv_out) return fail(SSW_EINVAL, "ssw_inverse_permutation: inv_out is NULL");
+  for (int p = 0; p < n; ++p) inv_out[sigma[p]] = p;
+  return SSW_OK;
+}
+
+int ssw_neighbor_mask(const int32_t* sigma, int n, int window, int causal, uint32_t* bits,
+                      void* stream) {
+  if (n < 0 || window < 1 || (causal != 0 && causal != 1))
+    return fail(SSW_EINVAL, "ssw_neighbor_mask: need n >= 0, window >= 1, causal in {0, 1}");
+  if (n > 65536) return fail(SSW_ESHAPE, "ssw_neighbor_mask: n must be <= 65536");
+  if (n == 0) return SSW_OK;
+  if (!bits) return fail(SSW_EINVAL, "ssw_neighbor_mask: bits is NULL");
+  if (!aligned(bits, 4) || (sigma && !aligned(sigma, 4)))
+    return fail(SSW_EALIGN, "ssw_neighbor_mask: sigma and bits must be 4-byte aligned");
+  const int w = window < n ? window : n;
+  hipError_t e = ssw::launch_neighbor_mask(sigma, n, w, causal != 0, bits, (hipStream_t)stream);
+  if (e != hipSuccess)
+    return fail(SSW_EHIP, std::string("ssw_neighbor_mask: launch failed: ") + hipGetErrorString(e));
+  return SSW_OK;
+}
+
+const char* ssw_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+"""CPU checks of libssw.so: it loads, exports every symbol include/ssw.h declares, its host-side
+permutation generator matches the oracle's bit for bit, and malformed calls are rejected with the
+documented status codes before anything reaches the GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import stochastic_sliding_window_amd as ssw
+import synth
+from oracle import make_permutation as oracle_perm, inverse_permutation as oracle_inv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssw.h")
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssw_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_symbols()
+    assert {"ssw_sa_forward", "ssw_swa_forward", "ssw_gated_sa_swa_forward"} <= set(names)
+    lib = ctypes.CDLL(ssw.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("wl", synth.WORKLOADS, ids=lambda w: w.name)
+def test_permutation_bit_exact_with_oracle_at_workload_sizes(wl):
+    for layer in range(wl.layers):
+        seed = synth.sigma_seed(wl.index, layer)
+        sigma, inv = ssw.make_permutation(seed, wl.n, with_inverse=True)
+        ref = oracle_perm(seed, wl.n)
+        assert sigma.dtype == np.int32
+        np.testing.assert_array_equal(sigma, ref)
+        np.testing.assert_array_equal(inv, oracle_inv(ref))
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 3, 17, 1000])
+def test_permutation_small_and_extreme_seeds(n):
+    for seed in (0, 1, 1234567, 2**64 - 1, 2**63):
+        np.testing.assert_array_equal(ssw.make_permutation(seed, n), oracle_perm(seed, n))
+
+
+def test_inverse_and_check():
+    s = ssw.make_permutation(42, 513)
+    inv = ssw.inverse_permutation(s)
+    np.testing.assert_array_equal(inv[s], np.arange(513))
+    assert ssw.check_permutation(s)
+    bad = s.copy()
+    bad[3] = bad[4]
+    assert not ssw.check_permutation(bad)
+    assert not ssw.check_permutation(np.array([0, 1, 5], dtype=np.int32))
+    assert not ssw.check_permutation(np.array([0, -1, 2], dtype=np.int32))
+    with pytest.raises(ssw.SSWError) as e:
+        ssw.inverse_permutation(bad)
+    assert e.value.status == -5
+    assert "permutation" in ssw.last_error()
+
+
+# ---- argument checking: every case below fails before any HIP call is made --------------------
+
+_lib = ctypes.CDLL(ssw.LIB_PATH)
+for _n in ("ssw_sa_forward", "ssw_swa_forward", "ssw_gated_sa_swa_forward"):
+    getattr(_lib, _n).argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 2 + \
+        [ctypes.c_void_p] * 2 + [ctypes.c_int] * 6 + [ctypes.c_void_p]
+    getattr(_lib, _n).restype = ctypes.c_int
+_lib.ssw_last_error.restype = ctypes.c_char_p
+
+P = 4096  # a fake, 16-byte aligned "device address": never dereferenced in these cases
+GOOD = dict(q=P, k=P, v=P, sigma=P, window=8, causal=1, gate=None, out=P,
+            B=1, n=64, Hq=4, Hkv=2, d=64, dtype=1)
+
+
+def _call(fn, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return getattr(_lib, fn)(a["q"], a["k"], a["v"], a["sigma"], a["window"], a["causal"],
+                             a["gate"], a["out"], a["B"], a["n"], a["Hq"], a["Hkv"], a["d"],
+                             a["dtype"], None)
+
+
+@pytest.mark.parametrize("fn", ["ssw_sa_forward", "ssw_swa_forward", "ssw_gated_sa_swa_forward"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=0), -1),
+    (dict(window=-3), -1),
+    (dict(causal=2), -1),
+    (dict(n=-1), -1),
+    (dict(Hkv=0), -1),
+    (dict(q=None), -1),
+    (dict(out=None), -1),
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(n=2**30, Hq=8, Hkv=2), -2),
+    (dict(d=96), -3),
+    (dict(d=256), -3),
+    (dict(dtype=7), -3),
+    (dict(q=P + 8), -4),
+    (dict(out=P + 4), -4),
+])
+def test_bad_arguments_rejected(fn, kw, status):
+    if fn == "ssw_swa_forward":
+        kw = dict(kw)
+        kw.setdefault("sigma", None)
+    assert _call(fn, **kw) == status
+    assert _lib.ssw_last_error().decode().startswith(fn)
+
+
+def test_entry_point_specific_checks():
+    assert _call("ssw_sa_forward", sigma=None) == -1
+    assert _call("ssw_sa_forward", sigma=P + 2) == -4
+    assert _call("ssw_swa_forward", sigma=P) == -1          # SWA takes no permutation
+    assert _call("ssw_gated_sa_swa_forward", gate=None) == -1
+    assert _call("ssw_gated_sa_swa_forward", gate=P + 1) == -4
+
+
+@pytest.mark.parametrize("fn", ["ssw_sa_forward", "ssw_swa_forward", "ssw_gated_sa_swa_forward"])
+def test_empty_calls_are_noops(fn):
+    sig = None if fn == "ssw_swa_forward" else P
+    for kw in (dict(B=0), dict(n=0)):
+        assert _call(fn, q=None, k=None, v=None, out=None, sigma=sig, **kw) == 0
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 8, 2, 64)
+    with pytest.raises(TypeError):
+        ssw.sa_forward(x, x[:, :, :1], x[:, :, :1], torch.arange(8, dtype=torch.int32), 4, True)
