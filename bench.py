@@ -1,0 +1,241 @@
+"""Benchmark: gated SA+SWA forward on one MI355X, long-context layer n = 32768, w = 128.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over one layer's synthetic input: one call of
+ssw_gated_sa_swa_forward, i.e. the SWA pass (leaves g_swa * Y_swa as the intermediate) followed by
+the SA pass (sigma-gathered window attention, adds g_sa * Y_sa at the scattered rows).
+Workload: B 1, n 32768, 32 query / 8 KV heads, d 128, bf16, causal, w 128; Q, K, V ~ N(0,1),
+gates sigmoid(N(0,1)), sigma from the seeded generator.  Inputs are resident in HBM before the
+timed region; three copies of every buffer are rotated so that no step finds its operands in
+the 256 MB last-level cache from the previous step.  Timing uses HIP events on the stream the
+kernels run on; the timed form of the entry point records events between its two kernels, which
+gives each kernel's average duration for the roofline.
+
+Prints ONE JSON line on stdout (details on stderr).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "gated SA+SWA fwd tokens/s + TFLOP/s, % roofline at n=32K, w=128 (1 GPU)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_pairs(n: int, w: int) -> int:
+    """Exact number of (query, key) pairs per (batch row, head) of causal SA (and of causal SWA):
+    every in-band pair of distinct slots is kept in exactly one direction, plus the n self pairs."""
+    w = min(w, n)
+    return n * w - w * (w - 1) // 2
+
+
+def pass_bytes(B, n, Hq, Hkv, d, elem, sa: bool, accumulate: bool) -> int:
+    """Algorithmic HBM bytes of one pass: each operand read once, the output written once."""
+    q = B * n * Hq * d * elem
+    kv = 2 * B * n * Hkv * d * elem
+    gate = B * n * Hq * 4
+    out = B * n * Hq * d * elem
+    sigma = n * 4 if sa else 0
+    return q + kv + gate + sigma + out * (2 if accumulate else 1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--window", type=int, default=128)
+    ap.add_argument("--sweep", action="store_true", help="also time SA / SWA alone at w 32, 64, 128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size (0 = auto)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); the multi-GPU path is "
+              "not built -- per-GPU shards are independent (see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import stochastic_sliding_window_amd as ssw
+    import synth
+
+    wl = synth.workload(4)
+    B, n, Hq, Hkv, d = wl.B, wl.n, wl.Hq, wl.Hkv, wl.d
+    w = args.window
+    causal = True
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs (host draw, then resident on the device)
+    t0 = time.perf_counter()
+    q, k, v = synth.qkv(synth.data_seed(4, 0), B, n, Hq, Hkv, d, wl.dtype)
+    g = synth.gates(synth.data_seed(4, 0), B, n, Hq)
+    log(f"inputs drawn in {time.perf_counter() - t0:.1f}s")
+    t0 = time.perf_counter()
+    sigma = ssw.make_permutation(synth.sigma_seed(4, 0), n)
+    sigma_ms = (time.perf_counter() - t0) * 1e3
+    ROT = 3
+    sets = []
+    for _ in range(ROT):
+        sets.append(dict(q=q.to(dev), k=k.to(dev), v=v.to(dev), gates=g.to(dev),
+                         out=torch.empty(B, n, Hq, d, dtype=q.dtype, device=dev),
+                         sigma=torch.from_numpy(sigma).to(dev)))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(s, ev=None):
+        ssw.gated_sa_swa_forward(s["q"], s["k"], s["v"], s["sigma"], w, causal, s["gates"],
+                                 out=s["out"], events=ev)
+
+    for i in range(args.warmup):
+        step(sets[i % ROT])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for trio in evs:          # materialise the (lazily created) HIP events before timing
+        for e in trio:
+            e.record(stream)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        step(sets[i % ROT], evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+    swa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    sa_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    # the same entry point without events, for comparison
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        step(sets[i % ROT])
+    end.record(stream)
+    torch.cuda.synchronize()
+    fused_ms = start.elapsed_time(end) / K
+
+    tokens = B * n
+    flops_pass = 4 * d * B * Hq * causal_pairs(n, w)
+    swa_bytes = pass_bytes(B, n, Hq, Hkv, d, 2, sa=False, accumulate=False)
+    sa_bytes = pass_bytes(B, n, Hq, Hkv, d, 2, sa=True, accumulate=True)
+    step_bytes = swa_bytes + sa_bytes
+    value = tokens / (ms_per_step * 1e-3)
+    tflops = 2 * flops_pass / (ms_per_step * 1e-3) / 1e12
+
+    dom = ("sa_pass", sa_ms, sa_bytes) if sa_ms >= swa_ms else ("swa_pass", swa_ms, swa_bytes)
+    achieved = dom[2] / (dom[1] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": dom[0], "bytes_per_launch": dom[2], "avg_launch_ms": round(dom[1], 4)}
+    log(f"step {ms_per_step * 1e3:.1f} us (without events {fused_ms * 1e3:.1f} us); "
+        f"SWA pass {swa_ms * 1e3:.1f} us = {swa_bytes / swa_ms / 1e6:.0f} GB/s, "
+        f"SA pass {sa_ms * 1e3:.1f} us = {sa_bytes / sa_ms / 1e6:.0f} GB/s; "
+        f"{value / 1e6:.1f} M tokens/s, {tflops:.1f} TFLOP/s; step bytes {step_bytes / 1e6:.0f} MB "
+        f"-> {step_bytes / ms_per_step / 1e6:.0f} GB/s ({step_bytes / ms_per_step / 1e6 / HBM_PEAK_GBS:.1%} of HBM)")
+
+    sweep = {}
+    if args.sweep:
+        for ww in (32, 64, 128):
+            for name in ("sa", "swa"):
+                def run(s, ww=ww, name=name):
+                    if name == "sa":
+                        ssw.sa_forward(s["q"], s["k"], s["v"], s["sigma"], ww, True, out=s["out"])
+                    else:
+                        ssw.swa_forward(s["q"], s["k"], s["v"], ww, True, out=s["out"])
+                for i in range(3):
+                    run(sets[i % ROT])
+                torch.cuda.synchronize()
+                start.record(stream)
+                for i in range(30):
+                    run(sets[i % ROT])
+                end.record(stream)
+                torch.cuda.synchronize()
+                t = start.elapsed_time(end) / 30
+                byt = pass_bytes(B, n, Hq, Hkv, d, 2, sa=(name == "sa"), accumulate=False) - B * n * Hq * 4
+                sweep[f"{name}_w{ww}_us"] = round(t * 1e3, 1)
+                log(f"  {name.upper()} alone w={ww}: {t * 1e3:.1f} us, {n / t / 1e3:.1f} M tok/s, "
+                    f"{byt / t / 1e6:.0f} GB/s, {4 * d * Hq * causal_pairs(n, ww) / t / 1e9:.1f} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(q, k, v, g, sigma, w, causal, args.cpu_rows)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: Q,K,V ~ N(0,1), gates sigmoid(N(0,1)), seeded sigma",
+        "config": {"workload": f"{wl.name} gated SA+SWA forward", "B": B, "n": n, "Hq": Hq,
+                   "Hkv": Hkv, "d": d, "window": w, "causal": causal},
+        "tflops": round(tflops, 2),
+        "tflops_frac_bf16": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "passes_us": {"swa_pass": round(swa_ms * 1e3, 1), "sa_pass": round(sa_ms * 1e3, 1),
+                      "step_without_events": round(fused_ms * 1e3, 1)},
+        "sigma_host_ms": round(sigma_ms, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if sweep:
+        line["sweep_us"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(q, k, v, g, sigma, w, causal, rows_req):
+    """The fp64 oracle, untuned, on a bounded sample of query rows of the same layer (both paths)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    n = q.shape[1]
+    rng = np.random.default_rng(0)
+    # warm the conversion caches the oracle builds from the tensors, then time a sample
+    qe, ke, ve = (t.float().numpy() for t in (q, k, v))
+    ge = g.double().numpy()
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.gated_forward(qe, ke, ve, sigma, w, causal, ge, rows)
+        return time.perf_counter() - t0
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        probe = rng.choice(n, size=16, replace=False)
+        t_probe = run(probe) / 16
+        rows = rows_req or max(16, min(4096, int(10.0 / max(t_probe, 1e-6))))
+        sample = rng.choice(n, size=rows, replace=False)
+        t = run(sample)
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    tps = rows / t
+    log(f"cpu oracle: {rows} rows in {t:.1f}s -> {tps:.1f} tokens/s (1 thread)")
+    return {"value": round(tps, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} random query rows of the same layer (all {q.shape[2]} heads, SA and "
+                      f"SWA paths, gated), fp64 NumPy, {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -83,12 +83,25 @@ int ssw_swa_forward(const void* q, const void* k, const void* v, const int32_t* 
 /* Gated dual path ([SA-ja] ゲート付き SA と SWA の組み合わせ):
  *   out = g_sa (.) SA(q, k, v; sigma, w, causal) + g_swa (.) SWA(q, k, v; w, causal).
  *   gates     device float32 [2, B, n, Hq], required.  Both paths use the same w and causal.
- * Two kernels run back to back on `stream`: the SA pass stores g_sa (.) Y_sa into `out`, then
- * the SWA pass reads it, adds g_swa (.) Y_swa and stores the sum.  In bf16 the SA partial is
- * rounded to bf16 once before the final rounding.  Other arguments as in ssw_sa_forward. */
+ * Two kernels run back to back on `stream`: the SWA pass leaves g_swa (.) Y_swa in `out` as an
+ * intermediate, then the SA pass reads it at each scattered row, adds g_sa (.) Y_sa and stores the
+ * sum.  For fp32 the intermediate is fp32.  For bf16 it is held, in the same two bytes per
+ * element, as fp16 bits of g_swa (.) Y_swa * 2^-8 (8x finer than bf16), so the result is in effect
+ * rounded to bf16 once; this needs |g_swa (.) Y_swa| < 1.6e7 (true whenever |V| < 1.6e7).
+ * Between the two passes `out` holds that intermediate, not a result.  Other arguments as in
+ * ssw_sa_forward. */
 int ssw_gated_sa_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma,
                              int window, int causal, const float* gates, void* out,
                              int B, int n, int Hq, int Hkv, int d, int dtype, void* stream);
+
+/* Same as ssw_gated_sa_swa_forward, and additionally records the given HIP events (hipEvent_t,
+ * each may be NULL) on `stream` before the SWA pass, between the passes and after the SA pass, so
+ * a caller can time each kernel.  Events must have been created by the caller. */
+int ssw_gated_sa_swa_forward_timed(const void* q, const void* k, const void* v,
+                                   const int32_t* sigma, int window, int causal,
+                                   const float* gates, void* out, int B, int n, int Hq, int Hkv,
+                                   int d, int dtype, void* stream, void* ev_start,
+                                   void* ev_between, void* ev_end);
 
 /* Host helpers (HOST pointers, no GPU needed). */
 

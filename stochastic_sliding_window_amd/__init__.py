@@ -9,7 +9,7 @@ The functions keep the C names without the ``ssw_`` prefix:
 
     sa_forward(q, k, v, sigma, window, causal, gate=None, out=None)
     swa_forward(q, k, v, window, causal, gate=None, out=None)
-    gated_sa_swa_forward(q, k, v, sigma, window, causal, gates, out=None)
+    gated_sa_swa_forward(q, k, v, sigma, window, causal, gates, out=None, events=None)
     make_permutation(seed, n) / inverse_permutation(sigma) / check_permutation(sigma)
     neighbor_mask(sigma, n, window, causal)
 
@@ -62,6 +62,8 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = fwd
         fn.restype = ctypes.c_int
+    lib.ssw_gated_sa_swa_forward_timed.argtypes = fwd + [vp, vp, vp]
+    lib.ssw_gated_sa_swa_forward_timed.restype = ctypes.c_int
     lib.ssw_make_permutation.argtypes = [ctypes.c_uint64, i32, i32p, i32p]
     lib.ssw_make_permutation.restype = ctypes.c_int
     lib.ssw_inverse_permutation.argtypes = [i32p, i32, i32p]
@@ -184,7 +186,8 @@ def _prep_gate(gate, shape, device):
 
 
 def sa_forward(q, k, v, sigma, window: int, causal: bool, gate=None, out=None):
-    """Stochastic Attention forward: out[b, sigma[p], h] = SWA_w in permuted space (ssw_sa_forward)."""
+    """Stochastic Attention forward (ssw_sa_forward): out[b, sigma[p], h] = window attention of
+    slot p in the permuted space, times ``gate`` [B, n, Hq] if given."""
     out = _prep(q, k, v, out)
     B, n, Hq, d = q.shape
     sigma = _prep_sigma(sigma, n, q.device)
@@ -206,18 +209,35 @@ def swa_forward(q, k, v, window: int, causal: bool, gate=None, out=None):
     return out
 
 
-def gated_sa_swa_forward(q, k, v, sigma, window: int, causal: bool, gates, out=None):
-    """Y = g_sa * SA + g_swa * SWA with gates [2, B, n, Hq] (ssw_gated_sa_swa_forward)."""
+def gated_sa_swa_forward(q, k, v, sigma, window: int, causal: bool, gates, out=None, events=None):
+    """Y = g_sa * SA + g_swa * SWA with gates [2, B, n, Hq] (ssw_gated_sa_swa_forward).
+
+    ``events``: optional (start, between, end) torch.cuda.Event triple recorded around the two
+    kernels (ssw_gated_sa_swa_forward_timed); each must have been recorded once already so that
+    its HIP event exists.
+    """
     out = _prep(q, k, v, out)
     B, n, Hq, d = q.shape
     sigma = _prep_sigma(sigma, n, q.device)
     if gates is None:
         raise ValueError("gates are required")
     gates = _prep_gate(gates, (2, B, n, Hq), q.device)
-    _check(_lib.ssw_gated_sa_swa_forward(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sigma),
-                                         int(window), int(bool(causal)), _dev_ptr(gates),
-                                         _dev_ptr(out), B, n, Hq, k.shape[2], d, _dtype_code(q),
-                                         _stream_handle(q)))
+    args = (_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sigma), int(window), int(bool(causal)),
+            _dev_ptr(gates), _dev_ptr(out), B, n, Hq, k.shape[2], d, _dtype_code(q),
+            _stream_handle(q))
+    if events is None:
+        _check(_lib.ssw_gated_sa_swa_forward(*args))
+    else:
+        handles = []
+        for e in events:
+            if e is None:
+                handles.append(None)
+                continue
+            h = e.cuda_event
+            if not h:
+                raise ValueError("record each event once before passing it (its HIP event is lazy)")
+            handles.append(ctypes.c_void_p(h))
+        _check(_lib.ssw_gated_sa_swa_forward_timed(*args, *handles))
     return out
 
 

@@ -7,9 +7,17 @@
 
 namespace ssw {
 
+// What a launch does with gate * Y at the output row.
+//   kEpiStore:      store it in the output dtype.
+//   kEpiPartial:    store it as the gated path's intermediate (SWA pass, sigma = identity only):
+//                   fp32 for fp32 outputs; for bf16 outputs, fp16 bits of Y * 2^-8 in the same
+//                   two bytes (8x finer than bf16, so the final result is rounded to bf16 once
+//                   in effect; holds |Y| < 1.6e7).
+//   kEpiAddPartial: read that intermediate, add, store in the output dtype (SA pass).
+enum Epilogue { kEpiStore = 0, kEpiPartial = 1, kEpiAddPartial = 2 };
+
 // One band-attention launch.  `perm` selects the stochastic (sigma-gathered) operator; without
-// it sigma is the identity (plain SWA).  `accumulate` adds gate * Y to the existing contents of
-// `out` instead of overwriting it (second pass of the gated path).
+// it sigma is the identity (plain SWA).
 struct BandLaunch {
   const void* q;
   const void* k;
@@ -22,7 +30,7 @@ struct BandLaunch {
   int window;            // already clamped to [1, n]
   bool causal;
   bool perm;
-  bool accumulate;
+  int epilogue;          // Epilogue
 };
 
 hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream);

@@ -38,6 +38,7 @@
 namespace ssw {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -50,6 +51,9 @@ constexpr int kColsWave = 32;
 constexpr int kColsWG = kColsWave * kWaves;
 constexpr int kChunk = 32;
 constexpr float kLazy = 8.0f;  // reference max may lag the true max by up to 2^8 (log2 units)
+// bf16 gated path: the SWA pass leaves g_swa * Y_swa in the output buffer as fp16 scaled by 2^-8
+constexpr float kPartialScale = 1.0f / 256.0f;
+constexpr float kPartialUnscale = 256.0f;
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -101,7 +105,7 @@ struct Params {
   float scale_log2;  // log2(e) / sqrt(d)
 };
 
-template <typename T, int D, bool PERM, bool SIGMASK, bool ACCUM>
+template <typename T, int D, bool PERM, bool SIGMASK, int EPI>
 __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
   using Lay = Layout<T, D>;
   constexpr bool kBf16 = Lay::kBf16;
@@ -305,18 +309,20 @@ __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
           sk[8 * half + 7] = bq[3];
         }
       }
-      float x[16];
+      // masked raw scores; the max is taken before scaling (the scale is positive)
+      float sm[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kc0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
         bool ok = interior || band_member(myslot, key, n, L, R);
         if constexpr (SIGMASK) ok = ok && sk[r] <= myorig;
-        x[r] = ok ? s[r] * prm.scale_log2 : -INFINITY;
+        sm[r] = ok ? s[r] : -INFINITY;
       }
-      float mx = x[0];
+      float mraw = sm[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 1; r < 16; ++r) mraw = fmaxf(mraw, sm[r]);
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+      const float mx = mraw * prm.scale_log2;  // log2 units
 
       const bool need = mx > m_ref + kLazy;
       const float m_new = need ? mx : m_ref;
@@ -324,13 +330,8 @@ __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
       m_ref = m_new;
       const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       float p[16];
-      float psum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(x[r] - m_use);
-        psum += p[r];
-      }
-      l_run = l_run * alpha + psum;
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[r], prm.scale_log2, -m_use));
       if (__ballot(need)) {
 #pragma unroll
         for (int t = 0; t < kOT; ++t) o[t] *= alpha;
@@ -344,6 +345,16 @@ __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
           pb0[e] = (__bf16)p[e];
           pb1[e] = (__bf16)p[8 + e];
         }
+        // The row sum is taken over the bf16-rounded weights that enter the P*V product, so the
+        // output is an exact convex combination of V rows with (slightly perturbed) weights.
+        float psum = 0.f;
+        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb0[e], pb0[e + 1]}, one2, psum, false);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb1[e], pb1[e + 1]}, one2, psum, false);
+        }
+        l_run = l_run * alpha + psum;
         const char* vp = Vst + (lane & 31) * Lay::kVRow + h32 * 16;
 #pragma unroll
         for (int t = 0; t < kOT; ++t) {
@@ -354,6 +365,10 @@ __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
           o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pb1, o[t], 0, 0, 0);
         }
       } else {
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) psum += p[r];
+        l_run = l_run * alpha + psum;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
@@ -380,34 +395,48 @@ __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int d0 = 32 * t + 8 * a + 4 * h32;
-      float y0 = o[t][4 * a + 0] * f;
-      float y1 = o[t][4 * a + 1] * f;
-      float y2 = o[t][4 * a + 2] * f;
-      float y3 = o[t][4 * a + 3] * f;
+      float y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) y[u] = o[t][4 * a + u] * f;
       if constexpr (kBf16) {
         u32x2* dst = (u32x2*)(orow + d0 * 2);
-        if constexpr (ACCUM) {
-          const u32x2 old = *dst;
-          y0 += __builtin_bit_cast(float, old[0] << 16);
-          y1 += __builtin_bit_cast(float, old[0] & 0xffff0000u);
-          y2 += __builtin_bit_cast(float, old[1] << 16);
-          y3 += __builtin_bit_cast(float, old[1] & 0xffff0000u);
+        if constexpr (EPI == kEpiPartial) {
+          // the gated intermediate: fp16 of y * 2^-8 (8x finer than bf16, range 1.6e7)
+          uint32_t w[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const _Float16 lo = (_Float16)(y[2 * u] * kPartialScale);
+            const _Float16 hi = (_Float16)(y[2 * u + 1] * kPartialScale);
+            w[u] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+          *dst = u32x2{w[0], w[1]};
+        } else {
+          if constexpr (EPI == kEpiAddPartial) {
+            const u32x2 old = *dst;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              y[2 * u] += (float)__builtin_bit_cast(_Float16, (uint16_t)(old[u] & 0xffffu)) *
+                          kPartialUnscale;
+              y[2 * u + 1] += (float)__builtin_bit_cast(_Float16, (uint16_t)(old[u] >> 16)) *
+                              kPartialUnscale;
+            }
+          }
+          const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[0]) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[1]) << 16);
+          const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[2]) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[3]) << 16);
+          *dst = u32x2{w0, w1};
         }
-        const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y0) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y1) << 16);
-        const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y2) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y3) << 16);
-        *dst = u32x2{w0, w1};
       } else {
+        // fp32: the gated intermediate is plain fp32
         f32x4* dst = (f32x4*)(orow + d0 * 4);
-        if constexpr (ACCUM) {
+        if constexpr (EPI == kEpiAddPartial) {
           const f32x4 old = *dst;
-          y0 += old[0];
-          y1 += old[1];
-          y2 += old[2];
-          y3 += old[3];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) y[u] += old[u];
         }
-        *dst = f32x4{y0, y1, y2, y3};
+        *dst = f32x4{y[0], y[1], y[2], y[3]};
       }
     }
   }
@@ -433,10 +462,10 @@ __global__ void neighbor_mask_kernel(const int32_t* sigma, int n, int L, int R, 
 }
 
 // ---- host-side dispatch
-template <typename T, int D, bool PERM, bool SIGMASK, bool ACCUM>
+template <typename T, int D, bool PERM, bool SIGMASK, int EPI>
 static hipError_t launch_t(const Params& prm, int ntiles, int nbg, hipStream_t stream) {
   dim3 grid(ntiles, nbg);
-  hipLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, ACCUM>), grid, dim3(kThreads), 0,
+  hipLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, EPI>), grid, dim3(kThreads), 0,
                      stream, prm);
   return hipGetLastError();
 }
@@ -444,16 +473,17 @@ static hipError_t launch_t(const Params& prm, int ntiles, int nbg, hipStream_t s
 template <typename T, int D>
 static hipError_t launch_d(const BandLaunch& a, const Params& prm, int ntiles, int nbg,
                            hipStream_t s) {
-  const bool sigmask = a.perm && a.causal;
+  // The SA pass of the gated path adds to the SWA pass's intermediate; nothing else combines.
   if (a.perm) {
-    if (sigmask)
-      return a.accumulate ? launch_t<T, D, true, true, true>(prm, ntiles, nbg, s)
-                          : launch_t<T, D, true, true, false>(prm, ntiles, nbg, s);
-    return a.accumulate ? launch_t<T, D, true, false, true>(prm, ntiles, nbg, s)
-                        : launch_t<T, D, true, false, false>(prm, ntiles, nbg, s);
+    const bool add = a.epilogue == kEpiAddPartial;
+    if (a.causal)
+      return add ? launch_t<T, D, true, true, kEpiAddPartial>(prm, ntiles, nbg, s)
+                 : launch_t<T, D, true, true, kEpiStore>(prm, ntiles, nbg, s);
+    return add ? launch_t<T, D, true, false, kEpiAddPartial>(prm, ntiles, nbg, s)
+               : launch_t<T, D, true, false, kEpiStore>(prm, ntiles, nbg, s);
   }
-  return a.accumulate ? launch_t<T, D, false, false, true>(prm, ntiles, nbg, s)
-                      : launch_t<T, D, false, false, false>(prm, ntiles, nbg, s);
+  return a.epilogue == kEpiPartial ? launch_t<T, D, false, false, kEpiPartial>(prm, ntiles, nbg, s)
+                                   : launch_t<T, D, false, false, kEpiStore>(prm, ntiles, nbg, s);
 }
 
 hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream) {

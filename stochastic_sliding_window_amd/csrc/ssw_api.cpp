@@ -104,7 +104,7 @@ ssw::BandLaunch make_launch(const void* q, const void* k, const void* v, const i
   a.window = window < n ? window : n;  // a band of n - 1 already covers every slot
   a.causal = causal != 0;
   a.perm = sigma != nullptr;
-  a.accumulate = false;
+  a.epilogue = ssw::kEpiStore;
   return a;
 }
 
@@ -115,7 +115,8 @@ extern "C" {
 int ssw_sa_forward(const void* q, const void* k, const void* v, const int32_t* sigma, int window,
                    int causal, const float* gate, void* out, int B, int n, int Hq, int Hkv, int d,
                    int dtype, void* stream) {
-  int st = check_forward("ssw_sa_forward", q, k, v, out, window, causal, B, n, Hq, Hkv, d, dtype);
+  const char* who = "ssw_sa_forward";
+  int st = check_forward(who, q, k, v, out, window, causal, B, n, Hq, Hkv, d, dtype);
   if (st != SSW_OK || B == 0 || n == 0) return st;
   if (!sigma) return fail(SSW_EINVAL, "ssw_sa_forward: sigma must be non-NULL");
   if (!aligned(sigma, 4) || (gate && !aligned(gate, 4)))
@@ -125,48 +126,79 @@ int ssw_sa_forward(const void* q, const void* k, const void* v, const int32_t* s
     st = check_sigma_on_device(sigma, n, s);
     if (st != SSW_OK) return st;
   }
-  return run("ssw_sa_forward",
-             make_launch(q, k, v, sigma, window, causal, gate, out, B, n, Hq, Hkv, d, dtype), s);
+  return run(who, make_launch(q, k, v, sigma, window, causal, gate, out, B, n, Hq, Hkv, d, dtype),
+             s);
 }
 
 int ssw_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma, int window,
                     int causal, const float* gate, void* out, int B, int n, int Hq, int Hkv, int d,
                     int dtype, void* stream) {
-  int st = check_forward("ssw_swa_forward", q, k, v, out, window, causal, B, n, Hq, Hkv, d, dtype);
+  const char* who = "ssw_swa_forward";
+  int st = check_forward(who, q, k, v, out, window, causal, B, n, Hq, Hkv, d, dtype);
   if (st != SSW_OK || B == 0 || n == 0) return st;
   if (sigma) return fail(SSW_EINVAL, "ssw_swa_forward: sigma must be NULL (identity)");
-  if (gate && !aligned(gate, 4)) return fail(SSW_EALIGN, "ssw_swa_forward: gate must be 4-byte aligned");
-  return run("ssw_swa_forward",
+  if (gate && !aligned(gate, 4))
+    return fail(SSW_EALIGN, "ssw_swa_forward: gate must be 4-byte aligned");
+  return run(who,
              make_launch(q, k, v, nullptr, window, causal, gate, out, B, n, Hq, Hkv, d, dtype),
              (hipStream_t)stream);
 }
 
-int ssw_gated_sa_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma,
-                             int window, int causal, const float* gates, void* out, int B, int n,
-                             int Hq, int Hkv, int d, int dtype, void* stream) {
-  int st = check_forward("ssw_gated_sa_swa_forward", q, k, v, out, window, causal, B, n, Hq, Hkv,
-                         d, dtype);
+static int gated(const char* who, const void* q, const void* k, const void* v,
+                 const int32_t* sigma, int window, int causal, const float* gates, void* out,
+                 int B, int n, int Hq, int Hkv, int d, int dtype, void* stream, void* ev_start,
+                 void* ev_between, void* ev_end) {
+  int st = check_forward(who, q, k, v, out, window, causal, B, n, Hq, Hkv, d, dtype);
   if (st != SSW_OK || B == 0 || n == 0) return st;
-  if (!sigma || !gates)
-    return fail(SSW_EINVAL, "ssw_gated_sa_swa_forward: sigma and gates must be non-NULL");
+  if (!sigma || !gates) return fail(SSW_EINVAL, std::string(who) + ": sigma and gates must be non-NULL");
   if (!aligned(sigma, 4) || !aligned(gates, 4))
-    return fail(SSW_EALIGN, "ssw_gated_sa_swa_forward: sigma and gates must be 4-byte aligned");
+    return fail(SSW_EALIGN, std::string(who) + ": sigma and gates must be 4-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   if (validate_requested()) {
     st = check_sigma_on_device(sigma, n, s);
     if (st != SSW_OK) return st;
   }
+  auto mark = [&](void* ev) -> int {
+    if (!ev) return SSW_OK;
+    hipError_t e = hipEventRecord((hipEvent_t)ev, s);
+    if (e != hipSuccess)
+      return fail(SSW_EHIP, std::string(who) + ": hipEventRecord failed: " + hipGetErrorString(e));
+    return SSW_OK;
+  };
   const float* g_sa = gates;
   const float* g_swa = gates + (size_t)B * n * Hq;
-  // pass 1: out = g_sa * Y_sa (scattered through sigma)
-  st = run("ssw_gated_sa_swa_forward",
-           make_launch(q, k, v, sigma, window, causal, g_sa, out, B, n, Hq, Hkv, d, dtype), s);
-  if (st != SSW_OK) return st;
-  // pass 2: out += g_swa * Y_swa (stream order makes the read-modify-write race-free)
-  ssw::BandLaunch a2 =
+  // Pass 1: the SWA pass leaves g_swa * Y_swa in `out` as the intermediate (fp32, or for bf16
+  // outputs fp16 bits of the value times 2^-8, so that the sum is in effect rounded to bf16 once).
+  ssw::BandLaunch a1 =
       make_launch(q, k, v, nullptr, window, causal, g_swa, out, B, n, Hq, Hkv, d, dtype);
-  a2.accumulate = true;
-  return run("ssw_gated_sa_swa_forward", a2, s);
+  a1.epilogue = ssw::kEpiPartial;
+  // Pass 2: the SA pass reads the intermediate at each scattered row sigma[p], adds
+  // g_sa * Y_sa and stores the result.  Stream order makes the read-modify-write race-free and
+  // sigma being a bijection means no two lanes touch the same row.
+  ssw::BandLaunch a2 =
+      make_launch(q, k, v, sigma, window, causal, g_sa, out, B, n, Hq, Hkv, d, dtype);
+  a2.epilogue = ssw::kEpiAddPartial;
+  if ((st = mark(ev_start)) != SSW_OK) return st;
+  if ((st = run(who, a1, s)) != SSW_OK) return st;
+  if ((st = mark(ev_between)) != SSW_OK) return st;
+  if ((st = run(who, a2, s)) != SSW_OK) return st;
+  return mark(ev_end);
+}
+
+int ssw_gated_sa_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma,
+                             int window, int causal, const float* gates, void* out, int B, int n,
+                             int Hq, int Hkv, int d, int dtype, void* stream) {
+  return gated("ssw_gated_sa_swa_forward", q, k, v, sigma, window, causal, gates, out, B, n, Hq,
+               Hkv, d, dtype, stream, nullptr, nullptr, nullptr);
+}
+
+int ssw_gated_sa_swa_forward_timed(const void* q, const void* k, const void* v,
+                                   const int32_t* sigma, int window, int causal,
+                                   const float* gates, void* out, int B, int n, int Hq, int Hkv,
+                                   int d, int dtype, void* stream, void* ev_start,
+                                   void* ev_between, void* ev_end) {
+  return gated("ssw_gated_sa_swa_forward_timed", q, k, v, sigma, window, causal, gates, out, B,
+               n, Hq, Hkv, d, dtype, stream, ev_start, ev_between, ev_end);
 }
 
 int ssw_make_permutation(uint64_t seed, int n, int32_t* sigma_out, int32_t* inv_out) {

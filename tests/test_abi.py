@@ -67,10 +67,13 @@ def test_inverse_and_check():
 # ---- argument checking: every case below fails before any HIP call is made --------------------
 
 _lib = ctypes.CDLL(ssw.LIB_PATH)
+_FWD_ARGS = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 2 + [ctypes.c_void_p] * 2 + \
+    [ctypes.c_int] * 6 + [ctypes.c_void_p]
 for _n in ("ssw_sa_forward", "ssw_swa_forward", "ssw_gated_sa_swa_forward"):
-    getattr(_lib, _n).argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 2 + \
-        [ctypes.c_void_p] * 2 + [ctypes.c_int] * 6 + [ctypes.c_void_p]
+    getattr(_lib, _n).argtypes = _FWD_ARGS
     getattr(_lib, _n).restype = ctypes.c_int
+_lib.ssw_gated_sa_swa_forward_timed.argtypes = _FWD_ARGS + [ctypes.c_void_p] * 3
+_lib.ssw_gated_sa_swa_forward_timed.restype = ctypes.c_int
 _lib.ssw_last_error.restype = ctypes.c_char_p
 
 P = 4096  # a fake, 16-byte aligned "device address": never dereferenced in these cases
@@ -81,12 +84,17 @@ GOOD = dict(q=P, k=P, v=P, sigma=P, window=8, causal=1, gate=None, out=P,
 def _call(fn, **kw):
     a = dict(GOOD)
     a.update(kw)
+    extra = (None, None, None) if fn.endswith("_timed") else ()
     return getattr(_lib, fn)(a["q"], a["k"], a["v"], a["sigma"], a["window"], a["causal"],
                              a["gate"], a["out"], a["B"], a["n"], a["Hq"], a["Hkv"], a["d"],
-                             a["dtype"], None)
+                             a["dtype"], None, *extra)
 
 
-@pytest.mark.parametrize("fn", ["ssw_sa_forward", "ssw_swa_forward", "ssw_gated_sa_swa_forward"])
+ALL_FWD = ["ssw_sa_forward", "ssw_swa_forward", "ssw_gated_sa_swa_forward",
+           "ssw_gated_sa_swa_forward_timed"]
+
+
+@pytest.mark.parametrize("fn", ALL_FWD)
 @pytest.mark.parametrize("kw,status", [
     (dict(window=0), -1),
     (dict(window=-3), -1),
@@ -117,9 +125,10 @@ def test_entry_point_specific_checks():
     assert _call("ssw_swa_forward", sigma=P) == -1          # SWA takes no permutation
     assert _call("ssw_gated_sa_swa_forward", gate=None) == -1
     assert _call("ssw_gated_sa_swa_forward", gate=P + 1) == -4
+    assert _call("ssw_gated_sa_swa_forward_timed", sigma=None) == -1
 
 
-@pytest.mark.parametrize("fn", ["ssw_sa_forward", "ssw_swa_forward", "ssw_gated_sa_swa_forward"])
+@pytest.mark.parametrize("fn", ALL_FWD)
 def test_empty_calls_are_noops(fn):
     sig = None if fn == "ssw_swa_forward" else P
     for kw in (dict(B=0), dict(n=0)):

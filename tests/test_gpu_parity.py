@@ -5,6 +5,11 @@ GPU and compares element by element with the oracle on the same values.  sigma i
 each side by its own implementation of the published generator and the two are asserted equal
 before use.  Bars: fp32 max |err| <= 1e-5; bf16 (fp32 accumulation, unit-variance V) max |err|
 <= 1.5e-2; neighbour sets and permutations bit-exact.
+
+The bf16 bar is applied to the bf16 OUTPUT.  Where the exact result has |Y| >= 4 the bf16 grid is
+2^-5 wide, so even the correctly rounded value can sit 2^-6 = 0.0156 away from it; there, and only
+there, the bar is raised by the excess of that half-spacing over 2^-7 (the half-spacing at the
+top of the unit range [2, 4)): tol(Y) = 1.5e-2 + max(0, h(Y) - 2^-7).
 """
 
 import sys
@@ -40,8 +45,27 @@ def _data(seed, B, n, Hq, Hkv, d, dt):
     return (q, k, v, g), (q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV))
 
 
-def _maxerr(gpu, ref):
-    return float(np.abs(gpu.detach().float().cpu().numpy().astype(np.float64) - ref).max())
+def _tol(ref, dt):
+    """Per-element bar (see the module docstring)."""
+    if dt == "f32":
+        return np.full(ref.shape, TOL["f32"])
+    mag = np.maximum(np.abs(ref), 1e-30)
+    half_spacing = np.exp2(np.floor(np.log2(mag)) - 8.0)
+    return TOL["bf16"] + np.maximum(0.0, half_spacing - 2.0 ** -7)
+
+
+def _maxerr(gpu, ref, dt=None):
+    """max |gpu - ref|; with dt, also asserts every element is within its bar."""
+    got = gpu.detach().float().cpu().numpy().astype(np.float64) if hasattr(gpu, "detach") else gpu
+    err = np.abs(got - ref)
+    if dt is not None:
+        tol = _tol(ref, dt)
+        bad = err > tol
+        if bad.any():
+            i = np.unravel_index(np.argmax(err - tol), err.shape)
+            raise AssertionError(f"{int(bad.sum())} elements over the bar; worst at {i}: "
+                                 f"got {got[i]}, oracle {ref[i]}, err {err[i]:.4e} > {tol[i]:.4e}")
+    return float(err.max())
 
 
 def _run_path(path, dev, sig_dev, w, causal):
@@ -86,9 +110,8 @@ def test_tiny_workload_fp32(path, causal):
     w = wl.windows[0]
     out = _run_path(path, dev, sig_dev, w, causal)
     torch.cuda.synchronize()
-    err = _maxerr(out, _oracle_path(path, host, sig, w, causal))
+    err = _maxerr(out, _oracle_path(path, host, sig, w, causal), "f32")
     _say(f"tiny {path} causal={causal}: max err {err:.3e}")
-    assert err <= TOL["f32"]
 
 
 # --------------------------------------------------------------------------------------------
@@ -116,9 +139,9 @@ def test_parity_shapes(shape, causal, dt):
     for path in ("sa", "swa", "gated"):
         out = _run_path(path, dev, sig_dev, w, causal)
         torch.cuda.synchronize()
-        err = _maxerr(out, _oracle_path(path, host, sig, w, causal))
-        _say(f"{shape} {dt} causal={causal} {path}: max err {err:.3e}")
-        assert err <= TOL[dt], (path, err)
+        _say(f"{shape} {dt} causal={causal} {path}")
+        err = _maxerr(out, _oracle_path(path, host, sig, w, causal), dt)
+        _say(f"   max err {err:.3e}")
 
 
 EDGES = [
@@ -143,8 +166,7 @@ def test_parity_edges(shape, causal, dt):
     for path in ("sa", "swa", "gated", "sa_gate"):
         out = _run_path(path, dev, sig_dev, w, causal)
         torch.cuda.synchronize()
-        err = _maxerr(out, _oracle_path(path, host, sig, w, causal))
-        assert err <= TOL[dt], (path, err)
+        _maxerr(out, _oracle_path(path, host, sig, w, causal), dt)
 
 
 def test_window_covering_sequence_is_full_attention_on_gpu():
@@ -161,6 +183,21 @@ def test_window_covering_sequence_is_full_attention_on_gpu():
             q.transpose(1, 2), kk.transpose(1, 2).contiguous(), vv.transpose(1, 2).contiguous(),
             is_causal=causal).transpose(1, 2)
         assert (out - ref).abs().max().item() <= 1e-5
+
+
+def test_timed_gated_call_matches_untimed():
+    B, n, Hq, Hkv, d, w = 1, 700, 8, 2, 128, 64
+    _, dev = _data(21, B, n, Hq, Hkv, d, "bf16")
+    sig_dev, _ = _sigma(22, n)
+    q, k, v, g = dev
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for e in evs:
+        e.record()
+    a = ssw.gated_sa_swa_forward(q, k, v, sig_dev, w, True, g)
+    b = ssw.gated_sa_swa_forward(q, k, v, sig_dev, w, True, g, events=evs)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert evs[0].elapsed_time(evs[1]) > 0 and evs[1].elapsed_time(evs[2]) > 0
 
 
 def test_empty_inputs_are_noops():
@@ -268,8 +305,7 @@ def test_full_size_workloads_sampled_rows(index):
                 torch.cuda.synchronize()
                 got = out[:, rows].float().cpu().numpy().astype(np.float64)
                 ref = _oracle_path(path, host, sig, w, True, rows)
-                err = float(np.abs(got - ref).max())
-                _say(f"workload {index} layer {layer} w={w} {path}: max err {err:.3e} "
-                     f"over {len(rows)} rows")
-                assert err <= TOL[wl.dtype], (index, layer, w, path, err)
+                _say(f"workload {index} layer {layer} w={w} {path} ({len(rows)} rows)")
+                err = _maxerr(got, ref, wl.dtype)
+                _say(f"   max err {err:.3e}")
                 assert torch.isfinite(out).all()
