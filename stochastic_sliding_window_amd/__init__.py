@@ -31,7 +31,9 @@ __all__ = [
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG_DIR, "libssw.so")
+# SSW_LIBRARY may name another build of the same library (e.g. one compiled with different tile
+# constants); by default the in-tree build is used.
+LIB_PATH = os.environ.get("SSW_LIBRARY") or os.path.join(_PKG_DIR, "libssw.so")
 
 F32 = 0
 BF16 = 1

@@ -36,22 +36,26 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libssw.so)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libssw.so; returns its path.  Always rebuilds."""
+def build(verbose: bool = False, out_path: str = LIB_PATH, defines=()) -> str:
+    """Compile every source and link libssw.so; returns its path.  Always rebuilds.
+
+    ``defines``: extra -D macros (tile-shape knobs of band_attn.hip, for tuning builds written
+    to ``out_path``)."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="ssw_build_") as tmp:
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc, *HIP_FLAGS, f"-I{INCLUDE}", *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *HIP_FLAGS, *[f"-D{d}" for d in defines], f"-I{INCLUDE}", *lang, "-c",
+                   os.path.join(CSRC, src), "-o", obj]
             _run(cmd, verbose)
             objs.append(obj)
         tmp_lib = os.path.join(tmp, "libssw.so")
         _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
-        shutil.copyfile(tmp_lib, LIB_PATH + ".tmp")
-        os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+        shutil.copyfile(tmp_lib, out_path + ".tmp")
+        os.replace(out_path + ".tmp", out_path)
+    return out_path
 
 
 def _run(cmd, verbose):
@@ -68,4 +72,10 @@ def _run(cmd, verbose):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("-o", default=LIB_PATH)
+    ap.add_argument("-D", action="append", default=[])
+    a = ap.parse_args()
+    print(build(verbose=a.v, out_path=a.o, defines=a.D))

@@ -45,7 +45,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kWaves = 8;
+#ifndef SSW_WAVES
+#define SSW_WAVES 8
+#endif
+#ifndef SSW_XCD_REMAP
+#define SSW_XCD_REMAP 1
+#endif
+constexpr int kWaves = SSW_WAVES;  // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kColsWave = 32;
 constexpr int kColsWG = kColsWave * kWaves;
@@ -103,7 +109,21 @@ struct Params {
   int B, n, Hq, Hkv, G;
   int L, R;          // band: key slots [p - L, p + R]
   float scale_log2;  // log2(e) / sqrt(d)
+  int ntiles;        // column tiles per (batch row, KV head)
+  int nblocks;       // ntiles * B * Hkv
 };
+
+// The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn, and each XCD has its own
+// L2.  Neighbouring column tiles of one (batch row, KV head) share most of their K/V band, so the
+// ids are renumbered to give every XCD a contiguous run of tiles: id i runs tile-major position
+// (i % 8) * (N / 8) + i / 8 (a bijection on the first 8 * floor(N / 8) ids; the rest keep theirs).
+__device__ __forceinline__ int xcd_local_order(int i, int nblocks) {
+#if SSW_XCD_REMAP
+  const int per = nblocks / 8;
+  if (i < per * 8) return (i % 8) * per + i / 8;
+#endif
+  return i;
+}
 
 template <typename T, int D, bool PERM, bool SIGMASK, int EPI>
 __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
@@ -121,12 +141,14 @@ __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
   const int R = prm.R;
   const int nG = n * G;
 
-  const int bg = blockIdx.y;
+  const int blk = xcd_local_order(blockIdx.x, prm.nblocks);
+  const int tile = blk % prm.ntiles;
+  const int bg = blk / prm.ntiles;
   const int b = bg / prm.Hkv;
   const int g = bg - b * prm.Hkv;
 
   // ---- columns of this workgroup / wave / lane
-  const int col0_wg = blockIdx.x * kColsWG;
+  const int col0_wg = tile * kColsWG;
   const int col0_w = col0_wg + wave * kColsWave;
   const int mycol = col0_w + (lane & 31);
   const bool colvalid = mycol < nG;
@@ -464,9 +486,10 @@ __global__ void neighbor_mask_kernel(const int32_t* sigma, int n, int L, int R, 
 // ---- host-side dispatch
 template <typename T, int D, bool PERM, bool SIGMASK, int EPI>
 static hipError_t launch_t(const Params& prm, int ntiles, int nbg, hipStream_t stream) {
-  dim3 grid(ntiles, nbg);
-  hipLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, EPI>), grid, dim3(kThreads), 0,
-                     stream, prm);
+  (void)ntiles;
+  (void)nbg;
+  hipLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, EPI>), dim3(prm.nblocks),
+                     dim3(kThreads), 0, stream, prm);
   return hipGetLastError();
 }
 
@@ -506,6 +529,8 @@ hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream) {
   const int64_t ncols = (int64_t)a.n * prm.G;
   const int ntiles = (int)((ncols + kColsWG - 1) / kColsWG);
   const int nbg = a.B * a.Hkv;
+  prm.ntiles = ntiles;
+  prm.nblocks = ntiles * nbg;
   if (a.dtype == 1) {
     return a.d == 128 ? launch_d<__bf16, 128>(a, prm, ntiles, nbg, stream)
                       : launch_d<__bf16, 64>(a, prm, ntiles, nbg, stream);

@@ -52,8 +52,11 @@ int check_forward(const char* who, const void* q, const void* k, const void* v, 
   if (d != 64 && d != 128) return fail(SSW_EDTYPE, w + ": head dim d must be 64 or 128");
   // every index the kernels form must stay inside int32 where they use int32
   const int64_t G = Hq / Hkv;
-  if ((int64_t)n * G > ((int64_t)1 << 31) - 4096 || (int64_t)B * Hkv >= 65536)
-    return fail(SSW_ESHAPE, w + ": n * Hq / Hkv must be <= 2^31 - 4096 and B * Hkv < 65536");
+  // (n * G / 128 column tiles) * B * Hkv workgroups must fit a 1-D grid
+  if ((int64_t)n * G > ((int64_t)1 << 31) - 4096 || (int64_t)B * Hkv >= 65536 ||
+      ((int64_t)n * G / 128 + 1) * B * Hkv >= ((int64_t)1 << 31))
+    return fail(SSW_ESHAPE, w + ": n * Hq / Hkv must be <= 2^31 - 4096, B * Hkv < 65536 and "
+                                "n * Hq * B / 128 < 2^31");
   if (B == 0 || n == 0) return SSW_OK;
   if (!q || !k || !v || !out) return fail(SSW_EINVAL, w + ": q, k, v and out must be non-NULL");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
