@@ -7,27 +7,30 @@
 // left of the band edge and past the sequence end are dropped); in causal mode a key is kept only
 // if sigma[q] <= sigma[p].  With sigma = identity the causal band collapses to [p - w + 1, p],
 // which this kernel exploits by taking the right band extent R = 0.  The output row of slot p is
-// written at original position sigma[p], optionally times a gate, optionally added to what is
-// there.
+// written at original position sigma[p], optionally times a gate, optionally combined with the
+// intermediate of the gated path.
 //
 // Mapping onto the chip.
-//   * One workgroup = 8 waves = one KV head of one batch row and 256 consecutive "columns",
-//     where a column is a (permuted slot, query head of the KV group) pair: column c is slot
-//     c / G, head c % G (G = Hq / Hkv).  So the G query heads sharing a KV head sit side by side
-//     and each K/V row staged in LDS serves all of them.
+//   * A workgroup owns one KV head of one batch row and 32 * waves consecutive "columns", where a
+//     column is a (permuted slot, query head of the KV group) pair: column c is slot c / G, head
+//     c % G (G = Hq / Hkv).  The G query heads sharing a KV head sit side by side, so each K/V
+//     row staged in LDS serves all of them.
 //   * Each wave owns 32 columns and computes S^T = K_chunk * Q^T with 32x32 MFMAs (rows = keys,
-//     columns = the wave's 32 columns), so every lane holds whole columns: the softmax row
-//     statistics of a column live in two lanes (lane l and l ^ 32) and need one cross-lane step.
-//   * Keys stream through LDS in chunks of 32, double-buffered: K rows are gathered through sigma
-//     straight from HBM (no permuted copy is ever written), stored in MFMA row order; V is stored
-//     transposed (bf16) so the P*V MFMA reads 8 consecutive keys per lane.
+//     columns = the wave's 32 columns), so every lane holds whole columns: the softmax statistics
+//     of a column live in two lanes (lane l and l ^ 32) and need one cross-lane step.
+//   * Keys stream through an LDS ring of kStages chunks of 32 keys.  Rows are gathered through
+//     sigma by buffer loads that write LDS directly (no registers, no permuted copy in HBM), so
+//     kStages - 1 chunks are in flight while one is consumed.  Keys past the sequence end read as
+//     zeros (the buffer range check).  K rows sit in MFMA row order with an XOR swizzle of their
+//     16-byte granules; V rows sit in key order, swizzled, and are read transposed with
+//     ds_read_b64_tr_b16 into the A operand of O^T = V^T * P^T.
 //   * The MFMA row -> key map is chosen so that the registers holding P^T after the softmax are
 //     already the B operand of the next MFMA (no register shuffles between the two products).
 //   * Softmax is online with a lazy reference maximum (rescale only when the running max grows
-//     by more than 2^8), and masks are evaluated per element only where a chunk touches the band
-//     edge or when the causal rule needs sigma.
-//   * Epilogue: divide by the row sum, multiply by the gate, scatter to row sigma[p] (store, or
-//     read-add-store for the second gated pass).
+//     by more than 2^8); the row sum is taken over the bf16-rounded weights the P*V product uses.
+//     Masks are evaluated per element only where a chunk touches the band edge or when the causal
+//     rule needs sigma.
+//   * Epilogue: divide by the row sum, multiply by the gate, scatter to row sigma[p].
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,19 +46,28 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+#define SSW_LDS __attribute__((address_space(3)))
 
-constexpr int kWave = 64;
 #ifndef SSW_WAVES
-#define SSW_WAVES 8
+#define SSW_WAVES 4
+#endif
+#ifndef SSW_STAGES
+#define SSW_STAGES 4
 #endif
 #ifndef SSW_XCD_REMAP
 #define SSW_XCD_REMAP 1
 #endif
+constexpr int kWave = 64;
 constexpr int kWaves = SSW_WAVES;  // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kColsWave = 32;
 constexpr int kColsWG = kColsWave * kWaves;
 constexpr int kChunk = 32;
+constexpr int kStages = SSW_STAGES;  // LDS ring depth: kStages - 1 chunks in flight
+constexpr int kSigCap = 2048;  // sigma entries held in LDS at a time (64 chunks)
+constexpr int kSegChunks = kSigCap / kChunk;
 constexpr float kLazy = 8.0f;  // reference max may lag the true max by up to 2^8 (log2 units)
 // bf16 gated path: the SWA pass leaves g_swa * Y_swa in the output buffer as fp16 scaled by 2^-8
 constexpr float kPartialScale = 1.0f / 256.0f;
@@ -74,30 +86,83 @@ __device__ __forceinline__ bool band_member(int p, int q, int n, int L, int R) {
   return q >= p - L && q <= p + R && q >= 0 && q < n;
 }
 
-// MFMA 32x32 output row r holds key rho(r) of the chunk; this is the inverse map (key -> row).
-// rho(8a + 4h + b) = 16(a / 2) + 8h + 4(a % 2) + b makes lane half h's registers 0..7 hold keys
-// 8h..8h+7 and registers 8..15 hold keys 16+8h..16+8h+7.
-__device__ __forceinline__ int key_to_row(int key) {
-  return 8 * (2 * (key >> 4) + ((key >> 2) & 1)) + 4 * ((key >> 3) & 1) + (key & 3);
+// MFMA 32x32 output row r holds key rho(r) of the chunk: rho(8a + 4h + b) = 16(a / 2) + 8h +
+// 4(a % 2) + b, so lane half h's registers 0..7 hold keys 8h..8h+7 and registers 8..15 hold keys
+// 16+8h..16+8h+7 -- exactly the k order of the B operand of the P*V product.
+__device__ __forceinline__ int row_to_key(int r) {
+  const int a = r >> 3;
+  return 16 * (a >> 1) + 8 * ((r >> 2) & 1) + 4 * (a & 1) + (r & 3);
+}
+
+// ---- raw buffer loads that write LDS directly (gfx950 buffer_load ... lds).  Issued as inline
+// asm so that the compiler does not serialise them with s_waitcnt vmcnt(0) before every LDS read;
+// the kernel waits for them itself with wait_vmcnt<N>.  Each instruction writes the 64 lanes'
+// data to consecutive LDS addresses starting at M0.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0, no swizzle
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);                // range checked per lane
+  r[3] = 0x00020000;                                                // 32-bit data format
+  return r;
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;  // any offset >= the range reads as zero
+
+__device__ __forceinline__ i32x4 uniform4(i32x4 r) {
+  i32x4 u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = __builtin_amdgcn_readfirstlane(r[i]);
+  return u;
+}
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  rsrc = uniform4(rsrc);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_addr),
+               "v"(voff), "s"(rsrc)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  rsrc = uniform4(rsrc);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds_addr),
+               "v"(voff), "s"(rsrc)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <typename T, int D>
 struct Layout {
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int kRowBytes = D * (int)sizeof(T);
-  static constexpr int kSegs = kRowBytes / 16;                     // 16-byte pieces per row
-  static constexpr int kPieces = kChunk * kSegs;                   // pieces per K (or V) chunk
-  static constexpr int kPPT = (kPieces + kThreads - 1) / kThreads;  // pieces per thread
-  static constexpr int kKRow = kRowBytes + 16;                     // padded K row (bytes)
-  static constexpr int kKBytes = kChunk * kKRow;
-  // bf16: V^T [D][32 keys] rows padded to 80 B; fp32: V [32 keys][D] rows padded by 16 B
-  static constexpr int kVRow = kBf16 ? (kChunk * 2 + 16) : (kRowBytes + 16);
-  static constexpr int kVBytes = kBf16 ? D * kVRow : kChunk * kVRow;
-  static constexpr int kSigOff = kKBytes + kVBytes;
-  static constexpr int kStage = kSigOff + kChunk * 4;
-  static_assert(kPieces % kWave == 0, "staging assumes whole waves");
-  static_assert(kStage % 16 == 0, "stage alignment");
+  static constexpr int kGran = kRowBytes / 16;  // 16-byte granules per row
+  static constexpr int kRowsPerDma = 1024 / kRowBytes;
+  static constexpr int kMatBytes = kChunk * kRowBytes;  // one K (or V) chunk
+  static constexpr int kDmaK = kMatBytes / 1024;        // DMA instructions per chunk and matrix
+  static constexpr int kDmaPerWave = 2 * kDmaK / kWaves;
+  static constexpr int kStageBytes = 2 * kMatBytes;
+  // ring depth: the configured number of stages, or fewer if they would not fit in 160 KB of LDS
+  static constexpr int kNS = kStages * kStageBytes + kSigCap * 4 <= 163840
+                                 ? kStages
+                                 : (163840 - kSigCap * 4) / kStageBytes;
+  static constexpr int kPF = kNS - 1;  // chunks in flight
+  static constexpr int kSigOff = kNS * kStageBytes;
+  static constexpr int kSmem = kSigOff + kSigCap * 4;
+  static_assert(kGran >= 8, "V swizzle needs 8 granules per row");
+  static_assert(kNS >= 2, "need at least two stages");
+  static_assert((2 * kDmaK) % kWaves == 0 && kDmaK % kDmaPerWave == 0, "DMA split");
 };
+
+// K rows (in MFMA row order) XOR their granule index with the row's low bits, so the lanes of an
+// A-operand read (consecutive rows, same granule) hit distinct banks.
+template <int GRAN>
+__device__ __forceinline__ int swz_k(int row) {
+  return row & (GRAN - 1);
+}
+// V rows (in key order) XOR with 2 * (key % 4): a transposed read touches 4 consecutive keys x
+// 2 granules per 16 lanes, which then cover 8 distinct granule slots.
+__device__ __forceinline__ int swz_v(int key) { return 2 * (key & 3); }
 
 struct Params {
   const char* q;
@@ -126,14 +191,17 @@ __device__ __forceinline__ int xcd_local_order(int i, int nblocks) {
 }
 
 template <typename T, int D, bool PERM, bool SIGMASK, int EPI>
-__global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void band_attn_kernel(Params prm) {
   using Lay = Layout<T, D>;
   constexpr bool kBf16 = Lay::kBf16;
-  __shared__ __attribute__((aligned(16))) char smem[2 * Lay::kStage];
+  __shared__ __attribute__((aligned(16))) char smem[Lay::kSmem];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;  // LDS byte address of smem
+  int* sig_lds = (int*)(smem + Lay::kSigOff);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps DMA setup scalar
   const int h32 = lane >> 5;  // lane half
   const int n = prm.n;
   const int G = prm.G;
@@ -155,7 +223,6 @@ __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
   const int mycol_c = colvalid ? mycol : nG - 1;
   const int myslot = mycol_c / G;
   const int h = g * G + (mycol_c - myslot * G);
-  const int myorig = PERM ? prm.sigma[myslot] : myslot;
 
   const bool wave_on = col0_w < nG;
   const int w_slo = col0_w / G;
@@ -168,7 +235,60 @@ __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
   const int c_first = (max(0, w_slo - L) - kbeg) / kChunk;
   const int c_last = (min(n - 1, w_shi + R) - kbeg) / kChunk;
 
-  // ---- Q fragment (B operand of S^T = K Q^T), kept in registers for the whole sweep
+  // ---- buffer resources of this (batch row, KV head) slice of K and V, and of sigma
+  const int64_t kv_row_stride = (int64_t)prm.Hkv * Lay::kRowBytes;
+  const int64_t kv_base = ((int64_t)b * n * prm.Hkv + g) * Lay::kRowBytes;
+  const uint32_t kv_range = (uint32_t)((int64_t)(n - 1) * kv_row_stride + Lay::kRowBytes);
+  const i32x4 rs_k = make_rsrc(prm.k + kv_base, kv_range);
+  const i32x4 rs_v = make_rsrc(prm.v + kv_base, kv_range);
+  const i32x4 rs_sig = make_rsrc(prm.sigma, PERM ? (uint32_t)n * 4u : 0u);
+
+  // sigma of keys [seg_key0, seg_key0 + 32 * nseg_chunks) into LDS (permuted operator only)
+  auto dma_sigma = [&](int seg_key0, int nseg_chunks) {
+    const int ninstr = (nseg_chunks * kChunk + 63) / 64;
+    for (int j = wave; j < ninstr; j += kWaves) {
+      const int key = seg_key0 + 64 * j + lane;
+      dma4(rs_sig, __builtin_amdgcn_readfirstlane(smem_lds + Lay::kSigOff + 256 * j),
+           key < n ? (uint32_t)key * 4u : kOutOfRange);
+    }
+  };
+
+  // this wave's share of the K and V rows of the chunk at key kc0, into ring stage `stage`
+  auto dma_chunk = [&](int kc0, int stage, int seg_key0) {
+#pragma unroll
+    for (int i = 0; i < Lay::kDmaPerWave; ++i) {
+      const int I = wave * Lay::kDmaPerWave + i;  // wave-uniform
+      const bool isv = I >= Lay::kDmaK;
+      const int blkid = isv ? I - Lay::kDmaK : I;
+      const int row = blkid * Lay::kRowsPerDma + lane / Lay::kGran;
+      const int gran = lane % Lay::kGran;
+      const int key = isv ? row : row_to_key(row);
+      const int src_gran = gran ^ (isv ? swz_v(key) : swz_k<Lay::kGran>(row));
+      const int q = kc0 + key;
+      int srcrow = -1;
+      if (q < n) srcrow = PERM ? sig_lds[q - seg_key0] : q;
+      const uint32_t voff =
+          srcrow >= 0 ? (uint32_t)(srcrow * kv_row_stride + src_gran * 16) : kOutOfRange;
+      const uint32_t lds = smem_lds + stage * Lay::kStageBytes + (isv ? Lay::kMatBytes : 0) +
+                           blkid * 1024;
+      dma16(isv ? rs_v : rs_k, __builtin_amdgcn_readfirstlane(lds), voff);
+    }
+  };
+
+  // ---- prologue: sigma of the first segment and of this lane's slot, then Q
+  const int nseg = (nchunks + kSegChunks - 1) / kSegChunks;
+  int myorig = myslot;
+  if constexpr (PERM) {
+    dma_sigma(kbeg, min(nchunks, kSegChunks));
+    myorig = prm.sigma[myslot];
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // the first chunks of the first segment go in flight before Q is loaded, so the two overlap
+#pragma unroll
+  for (int pf = 0; pf < Lay::kPF; ++pf)
+    if (pf < min(nchunks, kSegChunks)) dma_chunk(kbeg + pf * kChunk, pf, kbeg);
+
   const int64_t qrow_elems = (((int64_t)b * n + myorig) * prm.Hq + h) * D;
   constexpr int kQRegs = kBf16 ? D / 16 : D / 2;
   typedef typename std::conditional<kBf16, bf16x8, float>::type QFrag;
@@ -192,77 +312,9 @@ __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
     }
   }
 
-  // ---- staging helpers: thread tid stages key r = tid & 31 (same r for all its pieces)
-  const int st_r = tid & 31;
-  const int64_t kv_row_stride = (int64_t)prm.Hkv * Lay::kRowBytes;
-  const char* kbase = prm.k + ((int64_t)b * n * prm.Hkv + g) * Lay::kRowBytes;
-  const char* vbase = prm.v + ((int64_t)b * n * prm.Hkv + g) * Lay::kRowBytes;
-
-  auto load_sig = [&](int kc0) -> int {
-    const int key = kc0 + st_r;
-    if (key >= n) return -1;
-    return PERM ? prm.sigma[key] : key;
-  };
-
-  u32x4 kreg[Lay::kPPT];
-  u32x4 vreg[Lay::kPPT];
-  auto load_kv = [&](int srcrow) {
-#pragma unroll
-    for (int j = 0; j < Lay::kPPT; ++j) {
-      const int i = tid + j * kThreads;
-      kreg[j] = u32x4{0, 0, 0, 0};
-      vreg[j] = u32x4{0, 0, 0, 0};
-      if (i < Lay::kPieces && srcrow >= 0) {
-        const int seg = i >> 5;
-        const int64_t off = (int64_t)srcrow * kv_row_stride + seg * 16;
-        kreg[j] = *(const u32x4*)(kbase + off);
-        vreg[j] = *(const u32x4*)(vbase + off);
-      }
-    }
-  };
-
-  auto store_stage = [&](int stage, int srcrow) {
-    char* st = smem + stage * Lay::kStage;
-    char* Kst = st;
-    char* Vst = st + Lay::kKBytes;
-    int* Sst = (int*)(st + Lay::kSigOff);
-#pragma unroll
-    for (int j = 0; j < Lay::kPPT; ++j) {
-      const int i = tid + j * kThreads;
-      if (i < Lay::kPieces) {
-        const int seg = i >> 5;
-        *(u32x4*)(Kst + key_to_row(st_r) * Lay::kKRow + seg * 16) = kreg[j];
-        if constexpr (kBf16) {
-          // transpose 8 d-values of keys r (even) and r+1 (odd, the neighbouring lane) into
-          // V^T[8seg + e][r..r+1]: the even lane writes e = 0..3, the odd lane e = 4..7.
-          const bool odd = st_r & 1;
-          const u32x4 mine = vreg[j];
-          const uint32_t send0 = odd ? mine[0] : mine[2];
-          const uint32_t send1 = odd ? mine[1] : mine[3];
-          const uint32_t got0 = __shfl_xor((int)send0, 1);
-          const uint32_t got1 = __shfl_xor((int)send1, 1);
-          // even lane: own = (e01, e23) of key r, other = (e01, e23) of key r+1
-          // odd lane:  own = (e45, e67) of key r, other = (e45, e67) of key r-1
-          const uint32_t own0 = odd ? mine[2] : mine[0];
-          const uint32_t own1 = odd ? mine[3] : mine[1];
-          const uint32_t lo0 = odd ? got0 : own0;  // dword holding the even key's pair
-          const uint32_t hi0 = odd ? own0 : got0;  // dword holding the odd key's pair
-          const uint32_t lo1 = odd ? got1 : own1;
-          const uint32_t hi1 = odd ? own1 : got1;
-          const int e0 = odd ? 4 : 0;
-          const int kpair = st_r & ~1;
-          char* vt = Vst + (8 * seg + e0) * Lay::kVRow + kpair * 2;
-          *(uint32_t*)(vt + 0 * Lay::kVRow) = (lo0 & 0xffffu) | (hi0 << 16);
-          *(uint32_t*)(vt + 1 * Lay::kVRow) = (lo0 >> 16) | (hi0 & 0xffff0000u);
-          *(uint32_t*)(vt + 2 * Lay::kVRow) = (lo1 & 0xffffu) | (hi1 << 16);
-          *(uint32_t*)(vt + 3 * Lay::kVRow) = (lo1 >> 16) | (hi1 & 0xffff0000u);
-        } else {
-          *(u32x4*)(Vst + st_r * Lay::kVRow + seg * 16) = vreg[j];
-        }
-      }
-    }
-    if (tid < kChunk) Sst[tid] = srcrow >= 0 ? srcrow : 0x7fffffff;
-  };
+  // Q (and with it the first chunks) must have landed before the loop: waiting here, where the
+  // compiler sees it, keeps it from re-waiting for Q inside the loop.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- accumulators
   constexpr int kOT = D / 32;
@@ -272,138 +324,180 @@ __global__ __launch_bounds__(kThreads) void band_attn_kernel(Params prm) {
   float m_ref = -INFINITY;
   float l_run = 0.f;
 
-  // ---- prologue: chunk 0 into stage 0, sigma of chunk 1 in flight
-  int sig_next = load_sig(kbeg);
-  load_kv(sig_next);
-  store_stage(0, sig_next);
-  sig_next = nchunks > 1 ? load_sig(kbeg + kChunk) : -1;
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; ++c) {
+  // ---- one chunk of keys from ring stage `stage`
+  auto compute_chunk = [&](int c, int stage, int seg_key0) {
     const int kc0 = kbeg + c * kChunk;
-    const bool has_next = c + 1 < nchunks;
-    const int sig_c1 = sig_next;
-    if (has_next) load_kv(sig_c1);
-    if (c + 2 < nchunks) sig_next = load_sig(kc0 + 2 * kChunk);
+    const char* Kst = smem + stage * Lay::kStageBytes;
+    const char* Vst = Kst + Lay::kMatBytes;
+    const int r32 = lane & 31;
 
-    if (wave_on && c >= c_first && c <= c_last) {
-      const char* st = smem + (c & 1) * Lay::kStage;
-      const char* Kst = st;
-      const char* Vst = st + Lay::kKBytes;
-      const int* Sst = (const int*)(st + Lay::kSigOff);
-
-      // S^T[key rho(row)][col] = <K[key], Q[col]>
-      f32x16 s = zero16();
-      if constexpr (kBf16) {
-        const char* kp = Kst + (lane & 31) * Lay::kKRow + h32 * 16;
+    // S^T[key rho(row)][col] = <K[key], Q[col]>
+    f32x16 s = zero16();
+    if constexpr (kBf16) {
+      const char* kp = Kst + r32 * Lay::kRowBytes;
 #pragma unroll
-        for (int kb = 0; kb < D / 16; ++kb) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + kb * 32));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s, 0, 0, 0);
-        }
-      } else {
-        const char* kp = Kst + (lane & 31) * Lay::kKRow + h32 * (D / 2) * 4;
-#pragma unroll
-        for (int t4 = 0; t4 < D / 8; ++t4) {
-          const f32x4 a4 = *(const f32x4*)(kp + t4 * 16);
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            s = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[u], qf[4 * t4 + u], s, 0, 0, 0);
-        }
+      for (int kb = 0; kb < D / 16; ++kb) {
+        const int gr = (2 * kb + h32) ^ swz_k<Lay::kGran>(r32);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + gr * 16));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s, 0, 0, 0);
       }
-
-      // mask + scale.  Register r holds key kc0 + 16(r/8) + 8*h32 + r%8.
-      const bool interior = kc0 >= w_shi - L && kc0 + kChunk - 1 <= w_slo + R &&
-                            kc0 + kChunk - 1 < n;
-      int sk[16];
-      if constexpr (SIGMASK) {
+    } else {
+      const char* kp = Kst + r32 * Lay::kRowBytes;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const u32x4 a = *(const u32x4*)(Sst + 16 * half + 8 * h32);
-          const u32x4 bq = *(const u32x4*)(Sst + 16 * half + 8 * h32 + 4);
-          sk[8 * half + 0] = a[0];
-          sk[8 * half + 1] = a[1];
-          sk[8 * half + 2] = a[2];
-          sk[8 * half + 3] = a[3];
-          sk[8 * half + 4] = bq[0];
-          sk[8 * half + 5] = bq[1];
-          sk[8 * half + 6] = bq[2];
-          sk[8 * half + 7] = bq[3];
-        }
-      }
-      // masked raw scores; the max is taken before scaling (the scale is positive)
-      float sm[16];
+      for (int u = 0; u < D / 8; ++u) {
+        const int gr = (h32 * (D / 8) + u) ^ swz_k<Lay::kGran>(r32);
+        const f32x4 a4 = *(const f32x4*)(kp + gr * 16);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kc0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
-        bool ok = interior || band_member(myslot, key, n, L, R);
-        if constexpr (SIGMASK) ok = ok && sk[r] <= myorig;
-        sm[r] = ok ? s[r] : -INFINITY;
-      }
-      float mraw = sm[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mraw = fmaxf(mraw, sm[r]);
-      mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
-      const float mx = mraw * prm.scale_log2;  // log2 units
-
-      const bool need = mx > m_ref + kLazy;
-      const float m_new = need ? mx : m_ref;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-      m_ref = m_new;
-      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[r], prm.scale_log2, -m_use));
-      if (__ballot(need)) {
-#pragma unroll
-        for (int t = 0; t < kOT; ++t) o[t] *= alpha;
-      }
-
-      // O^T[d][col] += V^T[d][key] P^T[key][col]
-      if constexpr (kBf16) {
-        bf16x8 pb0, pb1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb0[e] = (__bf16)p[e];
-          pb1[e] = (__bf16)p[8 + e];
-        }
-        // The row sum is taken over the bf16-rounded weights that enter the P*V product, so the
-        // output is an exact convex combination of V rows with (slightly perturbed) weights.
-        float psum = 0.f;
-        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb0[e], pb0[e + 1]}, one2, psum, false);
-          psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb1[e], pb1[e + 1]}, one2, psum, false);
-        }
-        l_run = l_run * alpha + psum;
-        const char* vp = Vst + (lane & 31) * Lay::kVRow + h32 * 16;
-#pragma unroll
-        for (int t = 0; t < kOT; ++t) {
-          const bf16x8 a0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(vp + t * 32 * Lay::kVRow));
-          const bf16x8 a1 =
-              __builtin_bit_cast(bf16x8, *(const u32x4*)(vp + t * 32 * Lay::kVRow + 32));
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, pb0, o[t], 0, 0, 0);
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pb1, o[t], 0, 0, 0);
-        }
-      } else {
-        float psum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) psum += p[r];
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
-          const float* vrow = (const float*)(Vst + key * Lay::kVRow) + (lane & 31);
-#pragma unroll
-          for (int t = 0; t < kOT; ++t)
-            o[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * t], p[r], o[t], 0, 0, 0);
-        }
+        for (int e = 0; e < 4; ++e)
+          s = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[e], qf[4 * u + e], s, 0, 0, 0);
       }
     }
 
-    if (has_next) store_stage((c + 1) & 1, sig_c1);
-    __syncthreads();
+    // mask.  Register r holds key kc0 + 16(r/8) + 8*h32 + r%8.
+    const bool interior =
+        kc0 >= w_shi - L && kc0 + kChunk - 1 <= w_slo + R && kc0 + kChunk - 1 < n;
+    int sk[16];
+    if constexpr (SIGMASK) {
+      const int* sp = sig_lds + (kc0 - seg_key0);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const u32x4 a = *(const u32x4*)(sp + 16 * half + 8 * h32);
+        const u32x4 bq = *(const u32x4*)(sp + 16 * half + 8 * h32 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sk[8 * half + e] = (int)a[e];
+          sk[8 * half + 4 + e] = (int)bq[e];
+        }
+      }
+    }
+    // masked raw scores; the max is taken before scaling (the scale is positive)
+    float sm[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kc0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
+      bool ok = interior || band_member(myslot, key, n, L, R);
+      if constexpr (SIGMASK) ok = ok && sk[r] <= myorig;
+      sm[r] = ok ? s[r] : -INFINITY;
+    }
+    float mraw = sm[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mraw = fmaxf(mraw, sm[r]);
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+    const float mx = mraw * prm.scale_log2;  // log2 units
+
+    const bool need = mx > m_ref + kLazy;
+    const float m_new = need ? mx : m_ref;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+    m_ref = m_new;
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[r], prm.scale_log2, -m_use));
+    if (__ballot(need)) {
+#pragma unroll
+      for (int t = 0; t < kOT; ++t) o[t] *= alpha;
+    }
+
+    // O^T[d][col] += V^T[d][key] P^T[key][col]
+    if constexpr (kBf16) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[0][e] = (__bf16)p[e];
+        pb[1][e] = (__bf16)p[8 + e];
+      }
+      // The row sum is taken over the bf16-rounded weights that enter the P*V product, so the
+      // output is an exact convex combination of V rows with (slightly perturbed) weights.
+      float psum = 0.f;
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0][e], pb[0][e + 1]}, one2, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][e], pb[1][e + 1]}, one2, psum, false);
+      }
+      l_run = l_run * alpha + psum;
+      // Transposed V reads: lane j of 16-lane group grp reads 4 d-values of key
+      // 16t + 8*h32 + j/4 (+4) at d = 32db + 16(grp%2) + 4(j%4); the tr16 read hands lane i the
+      // i-th column of its group, which is the A operand row d = 32db + lane%32.
+      const int grp = lane >> 4;
+      const int j = lane & 15;
+      const int kr = 8 * h32 + (j >> 2);
+      const int dsub = 16 * (grp & 1) + 4 * (j & 3);
+      const SSW_LDS char* vbase = (const SSW_LDS char*)Vst;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int db = 0; db < kOT; ++db) {
+          const int d = 32 * db + dsub;
+          const int key0 = 16 * t + kr;
+          const int key1 = key0 + 4;
+          const int off0 =
+              key0 * Lay::kRowBytes + (((d >> 3) ^ swz_v(key0)) << 4) + ((d & 7) << 1);
+          const int off1 =
+              key1 * Lay::kRowBytes + (((d >> 3) ^ swz_v(key1)) << 4) + ((d & 7) << 1);
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)(vbase + off0));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)(vbase + off1));
+          // whole-vector casts only: building the operand element by element from the 16-bit
+          // lanes was miscompiled (only the first dword of each read survived)
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+          const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], o[db], 0, 0, 0);
+        }
+      }
+    } else {
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) psum += p[r];
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
+        const char* vrow = Vst + key * Lay::kRowBytes;
+#pragma unroll
+        for (int t = 0; t < kOT; ++t) {
+          const int d = 32 * t + r32;
+          const float vv =
+              *(const float*)(vrow + (((d >> 2) ^ swz_v(key)) << 4) + ((d & 3) << 2));
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, p[r], o[t], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- main loop over segments of at most kSegChunks chunks (one segment in practice)
+  for (int sg = 0; sg < nseg; ++sg) {
+    const int c0 = sg * kSegChunks;
+    const int segc = min(kSegChunks, nchunks - c0);
+    const int seg_key0 = kbeg + c0 * kChunk;
+    if (sg > 0) {
+      // drain the previous segment, bring in this one's sigma, then its first chunks
+      wait_vmcnt<0>();
+      __syncthreads();
+      if constexpr (PERM) {
+        dma_sigma(seg_key0, segc);
+        wait_vmcnt<0>();
+        __syncthreads();
+      }
+#pragma unroll
+      for (int pf = 0; pf < Lay::kPF; ++pf)
+        if (pf < segc) dma_chunk(seg_key0 + pf * kChunk, pf, seg_key0);
+    }
+
+    for (int cs = 0; cs < segc; ++cs) {
+      // this wave's DMAs for chunk cs are done once at most (Lay::kPF - 1) chunks' worth of its
+      // younger DMAs remain outstanding; near the end, wait for everything
+      if (cs + Lay::kPF - 1 < segc)
+        wait_vmcnt<Lay::kDmaPerWave * (Lay::kPF - 1)>();
+      else
+        wait_vmcnt<0>();
+      __syncthreads();  // every wave's DMAs for chunk cs landed; chunk cs - 1 fully consumed
+      if (cs + Lay::kPF < segc)
+        dma_chunk(seg_key0 + (cs + Lay::kPF) * kChunk, (cs + Lay::kPF) % Lay::kNS, seg_key0);
+      const int c = c0 + cs;
+      if (wave_on && c >= c_first && c <= c_last) compute_chunk(c, cs % Lay::kNS, seg_key0);
+    }
   }
 
   // ---- epilogue: normalise, gate, scatter to original row sigma[p]
@@ -485,28 +579,25 @@ __global__ void neighbor_mask_kernel(const int32_t* sigma, int n, int L, int R, 
 
 // ---- host-side dispatch
 template <typename T, int D, bool PERM, bool SIGMASK, int EPI>
-static hipError_t launch_t(const Params& prm, int ntiles, int nbg, hipStream_t stream) {
-  (void)ntiles;
-  (void)nbg;
+static hipError_t launch_t(const Params& prm, hipStream_t stream) {
   hipLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, EPI>), dim3(prm.nblocks),
                      dim3(kThreads), 0, stream, prm);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_d(const BandLaunch& a, const Params& prm, int ntiles, int nbg,
-                           hipStream_t s) {
+static hipError_t launch_d(const BandLaunch& a, const Params& prm, hipStream_t s) {
   // The SA pass of the gated path adds to the SWA pass's intermediate; nothing else combines.
   if (a.perm) {
     const bool add = a.epilogue == kEpiAddPartial;
     if (a.causal)
-      return add ? launch_t<T, D, true, true, kEpiAddPartial>(prm, ntiles, nbg, s)
-                 : launch_t<T, D, true, true, kEpiStore>(prm, ntiles, nbg, s);
-    return add ? launch_t<T, D, true, false, kEpiAddPartial>(prm, ntiles, nbg, s)
-               : launch_t<T, D, true, false, kEpiStore>(prm, ntiles, nbg, s);
+      return add ? launch_t<T, D, true, true, kEpiAddPartial>(prm, s)
+                 : launch_t<T, D, true, true, kEpiStore>(prm, s);
+    return add ? launch_t<T, D, true, false, kEpiAddPartial>(prm, s)
+               : launch_t<T, D, true, false, kEpiStore>(prm, s);
   }
-  return a.epilogue == kEpiPartial ? launch_t<T, D, false, false, kEpiPartial>(prm, ntiles, nbg, s)
-                                   : launch_t<T, D, false, false, kEpiStore>(prm, ntiles, nbg, s);
+  return a.epilogue == kEpiPartial ? launch_t<T, D, false, false, kEpiPartial>(prm, s)
+                                   : launch_t<T, D, false, false, kEpiStore>(prm, s);
 }
 
 hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream) {
@@ -527,16 +618,13 @@ hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream) {
   prm.R = (!a.perm && a.causal) ? 0 : a.window - 1;
   prm.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)a.d));
   const int64_t ncols = (int64_t)a.n * prm.G;
-  const int ntiles = (int)((ncols + kColsWG - 1) / kColsWG);
-  const int nbg = a.B * a.Hkv;
-  prm.ntiles = ntiles;
-  prm.nblocks = ntiles * nbg;
+  prm.ntiles = (int)((ncols + kColsWG - 1) / kColsWG);
+  prm.nblocks = prm.ntiles * a.B * a.Hkv;
   if (a.dtype == 1) {
-    return a.d == 128 ? launch_d<__bf16, 128>(a, prm, ntiles, nbg, stream)
-                      : launch_d<__bf16, 64>(a, prm, ntiles, nbg, stream);
+    return a.d == 128 ? launch_d<__bf16, 128>(a, prm, stream)
+                      : launch_d<__bf16, 64>(a, prm, stream);
   }
-  return a.d == 128 ? launch_d<float, 128>(a, prm, ntiles, nbg, stream)
-                    : launch_d<float, 64>(a, prm, ntiles, nbg, stream);
+  return a.d == 128 ? launch_d<float, 128>(a, prm, stream) : launch_d<float, 64>(a, prm, stream);
 }
 
 hipError_t launch_neighbor_mask(const int32_t* sigma, int n, int window, bool causal,
