@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "band_attn.h"
 
@@ -73,11 +74,40 @@ constexpr float kLazy = 8.0f;  // reference max may lag the true max by up to 2^
 constexpr float kPartialScale = 1.0f / 256.0f;
 constexpr float kPartialUnscale = 256.0f;
 
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{})
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
+}
+
+// Lanes l and l ^ 32 hold the same column.  v_permlane32_swap exchanges the upper half of one
+// register with the lower half of another in one VALU instruction; with both holding x, one ends
+// up as [x_lo, x_lo] and the other as [x_hi, x_hi], and combining them gives both lanes the
+// column total.  Inline asm: the compiler builtin's two results were folded into one when both
+// inputs were the same value, which dropped the combine.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
 }
 
 // Key membership in permuted-slot space.  The attention kernel and the neighbour-mask kernel use
@@ -150,7 +180,7 @@ struct Layout {
   static constexpr int kSigOff = kNS * kStageBytes;
   static constexpr int kSmem = kSigOff + kSigCap * 4;
   static_assert(kGran >= 8, "V swizzle needs 8 granules per row");
-  static_assert(kNS >= 2, "need at least two stages");
+  static_assert(kNS >= 3, "the software pipeline needs at least three stages");
   static_assert((2 * kDmaK) % kWaves == 0 && kDmaK % kDmaPerWave == 0, "DMA split");
 };
 
@@ -160,9 +190,21 @@ template <int GRAN>
 __device__ __forceinline__ int swz_k(int row) {
   return row & (GRAN - 1);
 }
-// V rows (in key order) XOR with 2 * (key % 4): a transposed read touches 4 consecutive keys x
-// 2 granules per 16 lanes, which then cover 8 distinct granule slots.
-__device__ __forceinline__ int swz_v(int key) { return 2 * (key & 3); }
+// V rows (in key order) XOR their granule index with a function of key % 4.  A transposed read
+// has each 16-lane group take 2 granules of 4 consecutive keys (and two groups together take 4
+// granules of the same 4 keys).  For 16-granule rows the XOR values 0, 6, 10, 12 spread both the
+// 16-lane and the 32-lane footprint over distinct bank slots (their residues mod 8 are distinct
+// and so are their bits 2..3); 8-granule rows use 0, 2, 4, 6.
+#ifndef SSW_VSWZ_WIDE
+#define SSW_VSWZ_WIDE 1
+#endif
+template <int GRAN>
+__device__ __forceinline__ int swz_v(int key) {
+  if constexpr (GRAN >= 16 && SSW_VSWZ_WIDE)
+    return (int)((0x0C0A0600u >> (8 * (key & 3))) & 0xFFu);
+  else
+    return 2 * (key & 3);
+}
 
 struct Params {
   const char* q;
@@ -253,26 +295,54 @@ void band_attn_kernel(Params prm) {
     }
   };
 
-  // this wave's share of the K and V rows of the chunk at key kc0, into ring stage `stage`
-  auto dma_chunk = [&](int kc0, int stage, int seg_key0) {
+  // this wave's share of the K and V rows of a chunk: per DMA instruction, the chunk-relative key
+  // this lane fetches and the byte offset of its (swizzled) source granule
+  constexpr int kDW = Lay::kDmaPerWave;
+  const uint32_t row_stride32 = (uint32_t)kv_row_stride;
+  int dma_key[kDW];
+  uint32_t dma_goff[kDW];
 #pragma unroll
-    for (int i = 0; i < Lay::kDmaPerWave; ++i) {
-      const int I = wave * Lay::kDmaPerWave + i;  // wave-uniform
+  for (int i = 0; i < kDW; ++i) {
+    const int I = wave * kDW + i;  // wave-uniform
+    const bool isv = I >= Lay::kDmaK;
+    const int blkid = isv ? I - Lay::kDmaK : I;
+    const int row = blkid * Lay::kRowsPerDma + lane / Lay::kGran;
+    const int gran = lane % Lay::kGran;
+    dma_key[i] = isv ? row : row_to_key(row);
+    dma_goff[i] = (uint32_t)((gran ^ (isv ? swz_v<Lay::kGran>(row) : swz_k<Lay::kGran>(row))) * 16);
+  }
+  // STAGE is a compile-time ring slot, so LDS addresses fold into instruction offsets.  The sigma
+  // reads for all of this wave's rows go out first (unconditionally: the segment's sigma buffer
+  // covers every key of its chunks), then the loads.
+  struct DmaRows {
+    int row[kDW];
+  };
+  auto dma_prep = [&](int kc0, int seg_key0) {
+    DmaRows r;
+#pragma unroll
+    for (int i = 0; i < kDW; ++i) {
+      const int q = kc0 + dma_key[i];
+      r.row[i] = PERM ? sig_lds[q - seg_key0] : q;
+    }
+    return r;
+  };
+  auto dma_issue = [&](int kc0, auto stage_c, const DmaRows& r) {
+    constexpr int STAGE = decltype(stage_c)::value;
+#pragma unroll
+    for (int i = 0; i < kDW; ++i) {
+      const int I = wave * kDW + i;  // wave-uniform
       const bool isv = I >= Lay::kDmaK;
       const int blkid = isv ? I - Lay::kDmaK : I;
-      const int row = blkid * Lay::kRowsPerDma + lane / Lay::kGran;
-      const int gran = lane % Lay::kGran;
-      const int key = isv ? row : row_to_key(row);
-      const int src_gran = gran ^ (isv ? swz_v(key) : swz_k<Lay::kGran>(row));
-      const int q = kc0 + key;
-      int srcrow = -1;
-      if (q < n) srcrow = PERM ? sig_lds[q - seg_key0] : q;
+      const int q = kc0 + dma_key[i];
       const uint32_t voff =
-          srcrow >= 0 ? (uint32_t)(srcrow * kv_row_stride + src_gran * 16) : kOutOfRange;
-      const uint32_t lds = smem_lds + stage * Lay::kStageBytes + (isv ? Lay::kMatBytes : 0) +
+          q < n ? (uint32_t)r.row[i] * row_stride32 + dma_goff[i] : kOutOfRange;
+      const uint32_t lds = smem_lds + STAGE * Lay::kStageBytes + (isv ? Lay::kMatBytes : 0) +
                            blkid * 1024;
       dma16(isv ? rs_v : rs_k, __builtin_amdgcn_readfirstlane(lds), voff);
     }
+  };
+  auto dma_chunk = [&](int kc0, auto stage_c, int seg_key0) {
+    dma_issue(kc0, stage_c, dma_prep(kc0, seg_key0));
   };
 
   // ---- prologue: sigma of the first segment and of this lane's slot, then Q
@@ -285,9 +355,9 @@ void band_attn_kernel(Params prm) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // the first chunks of the first segment go in flight before Q is loaded, so the two overlap
-#pragma unroll
-  for (int pf = 0; pf < Lay::kPF; ++pf)
-    if (pf < min(nchunks, kSegChunks)) dma_chunk(kbeg + pf * kChunk, pf, kbeg);
+  static_for<Lay::kPF>([&](auto pf) {
+    if (pf() < min(nchunks, kSegChunks)) dma_chunk(kbeg + pf() * kChunk, pf, kbeg);
+  });
 
   const int64_t qrow_elems = (((int64_t)b * n + myorig) * prm.Hq + h) * D;
   constexpr int kQRegs = kBf16 ? D / 16 : D / 2;
@@ -324,34 +394,64 @@ void band_attn_kernel(Params prm) {
   float m_ref = -INFINITY;
   float l_run = 0.f;
 
-  // ---- one chunk of keys from ring stage `stage`
-  auto compute_chunk = [&](int c, int stage, int seg_key0) {
-    const int kc0 = kbeg + c * kChunk;
-    const char* Kst = smem + stage * Lay::kStageBytes;
-    const char* Vst = Kst + Lay::kMatBytes;
-    const int r32 = lane & 31;
+  // ---- per-lane LDS offsets of the MFMA operands within a stage (the same for every chunk)
+  const int r32 = lane & 31;
+  constexpr int kKReads = kBf16 ? D / 16 : D / 8;  // 16-byte K reads per chunk
+  int k_off[kKReads];
+#pragma unroll
+  for (int u = 0; u < kKReads; ++u) {
+    const int gran = kBf16 ? 2 * u + h32 : h32 * (D / 8) + u;
+    k_off[u] = r32 * Lay::kRowBytes + ((gran ^ swz_k<Lay::kGran>(r32)) << 4);
+  }
+  // bf16: transposed V reads.  Lane j of 16-lane group grp reads 4 d-values of key
+  // 16t + 8*h32 + j/4 (+4 for the upper half) at d = 32db + 16(grp%2) + 4(j%4); the tr16 read then
+  // hands lane i of the group column i, i.e. the A operand row d = 32db + lane%32.  Key % 4 (and
+  // so the swizzle) is the same for every (t, half), which only add 16t + 4*half rows: one base
+  // offset per d block, the rest are instruction offsets.
+  int v_off[kOT];
+  if constexpr (kBf16) {
+    const int grp = lane >> 4;
+    const int j = lane & 15;
+    const int dsub = 16 * (grp & 1) + 4 * (j & 3);
+    const int key = 8 * h32 + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < kOT; ++db) {
+      const int d = 32 * db + dsub;
+      v_off[db] = Lay::kMatBytes + key * Lay::kRowBytes +
+                  (((d >> 3) ^ swz_v<Lay::kGran>(key)) << 4) + ((d & 7) << 1);
+    }
+  }
 
-    // S^T[key rho(row)][col] = <K[key], Q[col]>
+  // ---- one chunk of keys from ring stage `stage`
+  // S^T[key rho(row)][col] = <K[key], Q[col]> for the chunk in ring slot STAGE
+  auto compute_s = [&](auto stage_c) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    const char* Kst = smem + STAGE * Lay::kStageBytes;
     f32x16 s = zero16();
     if constexpr (kBf16) {
-      const char* kp = Kst + r32 * Lay::kRowBytes;
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
-        const int gr = (2 * kb + h32) ^ swz_k<Lay::kGran>(r32);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + gr * 16));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kst + k_off[kb]));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s, 0, 0, 0);
       }
     } else {
-      const char* kp = Kst + r32 * Lay::kRowBytes;
 #pragma unroll
       for (int u = 0; u < D / 8; ++u) {
-        const int gr = (h32 * (D / 8) + u) ^ swz_k<Lay::kGran>(r32);
-        const f32x4 a4 = *(const f32x4*)(kp + gr * 16);
+        const f32x4 a4 = *(const f32x4*)(Kst + k_off[u]);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           s = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[e], qf[4 * u + e], s, 0, 0, 0);
       }
     }
+    return s;
+  };
+
+  // mask, online softmax and O^T += V^T P^T for chunk c (ring slot STAGE) given its scores
+  auto softmax_pv = [&](int c, auto stage_c, int seg_key0, const f32x16& s) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    const int kc0 = kbeg + c * kChunk;
+    const char* Kst = smem + STAGE * Lay::kStageBytes;
+    const char* Vst = Kst + Lay::kMatBytes;
 
     // mask.  Register r holds key kc0 + 16(r/8) + 8*h32 + r%8.
     const bool interior =
@@ -370,19 +470,34 @@ void band_attn_kernel(Params prm) {
         }
       }
     }
-    // masked raw scores; the max is taken before scaling (the scale is positive)
+    // masked raw scores; the max is taken before scaling (the scale is positive).  Branch-free:
+    // interior chunks need only the causal test; edge chunks also test the lane's band, held as a
+    // bit mask over the chunk's 32 key offsets.
     float sm[16];
+    if (interior) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kc0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
-      bool ok = interior || band_member(myslot, key, n, L, R);
-      if constexpr (SIGMASK) ok = ok && sk[r] <= myorig;
-      sm[r] = ok ? s[r] : -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        bool ok = true;
+        if constexpr (SIGMASK) ok = sk[r] <= myorig;
+        sm[r] = ok ? s[r] : -INFINITY;
+      }
+    } else {
+      const int a = max(max(myslot - L, 0) - kc0, 0);         // first valid offset (may be > 31)
+      const int z = min(min(myslot + R, n - 1) - kc0, 31);     // last valid offset (may be < 0)
+      const uint32_t upto = z < 0 ? 0u : (0xFFFFFFFFu >> (31 - z));
+      const uint32_t from = a > 31 ? 0u : (0xFFFFFFFFu << a);
+      const uint32_t bm = (upto & from) >> (8 * h32);          // bit 16(r/8) + r%8 for register r
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        bool ok = (bm >> (16 * (r >> 3) + (r & 7))) & 1u;
+        if constexpr (SIGMASK) ok = ok & (sk[r] <= myorig);
+        sm[r] = ok ? s[r] : -INFINITY;
+      }
     }
     float mraw = sm[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mraw = fmaxf(mraw, sm[r]);
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+    mraw = pair_max(mraw);
     const float mx = mraw * prm.scale_log2;  // log2 units
 
     const bool need = mx > m_ref + kLazy;
@@ -417,27 +532,15 @@ void band_attn_kernel(Params prm) {
         psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][e], pb[1][e + 1]}, one2, psum, false);
       }
       l_run = l_run * alpha + psum;
-      // Transposed V reads: lane j of 16-lane group grp reads 4 d-values of key
-      // 16t + 8*h32 + j/4 (+4) at d = 32db + 16(grp%2) + 4(j%4); the tr16 read hands lane i the
-      // i-th column of its group, which is the A operand row d = 32db + lane%32.
-      const int grp = lane >> 4;
-      const int j = lane & 15;
-      const int kr = 8 * h32 + (j >> 2);
-      const int dsub = 16 * (grp & 1) + 4 * (j & 3);
-      const SSW_LDS char* vbase = (const SSW_LDS char*)Vst;
+      const SSW_LDS char* vbase = (const SSW_LDS char*)Kst;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int db = 0; db < kOT; ++db) {
-          const int d = 32 * db + dsub;
-          const int key0 = 16 * t + kr;
-          const int key1 = key0 + 4;
-          const int off0 =
-              key0 * Lay::kRowBytes + (((d >> 3) ^ swz_v(key0)) << 4) + ((d & 7) << 1);
-          const int off1 =
-              key1 * Lay::kRowBytes + (((d >> 3) ^ swz_v(key1)) << 4) + ((d & 7) << 1);
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)(vbase + off0));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)(vbase + off1));
+          const SSW_LDS char* vp = vbase + v_off[db] + 16 * t * Lay::kRowBytes;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)vp);
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)(vp + 4 * Lay::kRowBytes));
           // whole-vector casts only: building the operand element by element from the 16-bit
           // lanes was miscompiled (only the first dword of each read survived)
           const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
@@ -458,8 +561,8 @@ void band_attn_kernel(Params prm) {
 #pragma unroll
         for (int t = 0; t < kOT; ++t) {
           const int d = 32 * t + r32;
-          const float vv =
-              *(const float*)(vrow + (((d >> 2) ^ swz_v(key)) << 4) + ((d & 3) << 2));
+          const float vv = *(const float*)(vrow + (((d >> 2) ^ swz_v<Lay::kGran>(key)) << 4) +
+                                           ((d & 3) << 2));
           o[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, p[r], o[t], 0, 0, 0);
         }
       }
@@ -480,28 +583,55 @@ void band_attn_kernel(Params prm) {
         wait_vmcnt<0>();
         __syncthreads();
       }
-#pragma unroll
-      for (int pf = 0; pf < Lay::kPF; ++pf)
-        if (pf < segc) dma_chunk(seg_key0 + pf * kChunk, pf, seg_key0);
+      static_for<Lay::kPF>([&](auto pf) {
+        if (pf() < segc) dma_chunk(seg_key0 + pf() * kChunk, pf, seg_key0);
+      });
     }
 
-    for (int cs = 0; cs < segc; ++cs) {
-      // this wave's DMAs for chunk cs are done once at most (Lay::kPF - 1) chunks' worth of its
-      // younger DMAs remain outstanding; near the end, wait for everything
-      if (cs + Lay::kPF - 1 < segc)
-        wait_vmcnt<Lay::kDmaPerWave * (Lay::kPF - 1)>();
-      else
-        wait_vmcnt<0>();
-      __syncthreads();  // every wave's DMAs for chunk cs landed; chunk cs - 1 fully consumed
-      if (cs + Lay::kPF < segc)
-        dma_chunk(seg_key0 + (cs + Lay::kPF) * kChunk, (cs + Lay::kPF) % Lay::kNS, seg_key0);
-      const int c = c0 + cs;
-      if (wave_on && c >= c_first && c <= c_last) compute_chunk(c, cs % Lay::kNS, seg_key0);
+    // Software pipeline: while chunk cs is consumed (softmax + P*V from its V), the scores of
+    // chunk cs + 1 are already computed from its K, so each wave has independent MFMA work to
+    // overlap with the softmax VALU work.  Chunk cs + kPF is fetched meanwhile.
+    auto active = [&](int c) { return wave_on && c >= c_first && c <= c_last; };
+    if (Lay::kPF - 1 < segc)
+      wait_vmcnt<Lay::kDmaPerWave * (Lay::kPF - 1)>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    f32x16 s_cur = zero16();
+    if (active(c0)) s_cur = compute_s(std::integral_constant<int, 0>{});
+
+    // unrolled by the ring depth so that every chunk's ring slot is a compile-time constant
+    for (int cs0 = 0; cs0 < segc; cs0 += Lay::kNS) {
+      static_for<Lay::kNS>([&](auto u) {
+        const int cs = cs0 + u();
+        if (cs < segc) {
+          constexpr int kNext = (u() + 1) % Lay::kNS;
+          constexpr int kFetch = (u() + Lay::kPF) % Lay::kNS;
+          const bool fetch = cs + Lay::kPF < segc;
+          DmaRows rows;
+          if (fetch) rows = dma_prep(seg_key0 + (cs + Lay::kPF) * kChunk, seg_key0);
+          // chunk cs + 1 must have landed: at most (kPF - 2) younger chunks of this wave's DMAs
+          // may still be outstanding; near the end, wait for everything
+          if (cs + Lay::kPF - 1 < segc)
+            wait_vmcnt<Lay::kDmaPerWave * (Lay::kPF - 2)>();
+          else
+            wait_vmcnt<0>();
+          __syncthreads();  // every wave's DMAs for chunk cs + 1 landed; chunk cs - 1 consumed
+          if (fetch)
+            dma_issue(seg_key0 + (cs + Lay::kPF) * kChunk, std::integral_constant<int, kFetch>{},
+                      rows);
+          f32x16 s_next = zero16();
+          if (cs + 1 < segc && active(c0 + cs + 1))
+            s_next = compute_s(std::integral_constant<int, kNext>{});
+          if (active(c0 + cs)) softmax_pv(c0 + cs, u, seg_key0, s_cur);
+          s_cur = s_next;
+        }
+      });
     }
   }
 
   // ---- epilogue: normalise, gate, scatter to original row sigma[p]
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (!colvalid) return;
   float f = 1.0f / l_tot;
   if (prm.gate) f *= prm.gate[((int64_t)b * n + myorig) * prm.Hq + h];
