@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 METRIC = "gated SA+SWA fwd tokens/s + TFLOP/s, % roofline at n=32K, w=128 (1 GPU)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+COPY_BYTES = 512 << 20
 
 
 def log(*a):
@@ -134,6 +135,8 @@ def main():
     torch.cuda.synchronize()
     fused_ms = start.elapsed_time(end) / K
 
+    copy_gbs = copy_bandwidth(dev, stream, start, end)
+
     tokens = B * n
     flops_pass = 4 * d * B * Hq * causal_pairs(n, w)
     swa_bytes = pass_bytes(B, n, Hq, Hkv, d, 2, sa=False, accumulate=False)
@@ -145,7 +148,7 @@ def main():
     dom = ("sa_pass", sa_ms, sa_bytes) if sa_ms >= swa_ms else ("swa_pass", swa_ms, swa_bytes)
     achieved = dom[2] / (dom[1] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom[0]),
                 "kernel": dom[0], "bytes_per_launch": dom[2], "avg_launch_ms": round(dom[1], 4)}
     log(f"step {ms_per_step * 1e3:.1f} us (without events {fused_ms * 1e3:.1f} us); "
         f"SWA pass {swa_ms * 1e3:.1f} us = {swa_bytes / swa_ms / 1e6:.0f} GB/s, "
@@ -193,12 +196,55 @@ def main():
         "passes_us": {"swa_pass": round(swa_ms * 1e3, 1), "sa_pass": round(sa_ms * 1e3, 1),
                       "step_without_events": round(fused_ms * 1e3, 1)},
         "sigma_host_ms": round(sigma_ms, 2),
+        "copy_gbs": round(copy_gbs, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     if sweep:
         line["sweep_us"] = sweep
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE counter runs
+    (scaled by the plain-copy calibration), or None when the kernel source has changed since the
+    counters were taken (or no counters were taken for it)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_n32768_w128.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in rec["sources_hashed"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["kernel_sha256"]:
+        log(f"counter figures in {os.path.basename(path)} are for an older kernel: traffic = null")
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
+def copy_bandwidth(dev, stream, start, end, nbytes=COPY_BYTES, reps=10):
+    """Read+write GB/s of a plain elementwise copy (int32 negate) of `nbytes` HBM-resident bytes.
+
+    Context for the roofline (what a streaming kernel reaches on this device), and the known-size
+    kernel that scales the FETCH_SIZE / WRITE_SIZE counters in profiled runs."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t = start.elapsed_time(end) / reps
+    gbs = 2 * nbytes / (t * 1e-3) / 1e9
+    log(f"plain copy of {nbytes >> 20} MiB: {t * 1e3:.1f} us -> {gbs:.0f} GB/s (read + write)")
+    del src, dst
+    return gbs
 
 
 def cpu_baseline(q, k, v, g, sigma, w, causal, rows_req):
@@ -222,9 +268,9 @@ def cpu_baseline(q, k, v, g, sigma, w, causal, rows_req):
     if ctx:
         ctx.__enter__()
     try:
-        probe = rng.choice(n, size=16, replace=False)
-        t_probe = run(probe) / 16
-        rows = rows_req or max(16, min(4096, int(10.0 / max(t_probe, 1e-6))))
+        run(rng.choice(n, size=16, replace=False))          # first call pays one-off set-up
+        t_probe = run(rng.choice(n, size=64, replace=False)) / 64
+        rows = rows_req or max(64, min(32768, int(12.0 / max(t_probe, 1e-6))))
         sample = rng.choice(n, size=rows, replace=False)
         t = run(sample)
     finally:

@@ -23,6 +23,12 @@ import os
 from typing import Optional
 
 import numpy as np
+# torch first: it loads its bundled HIP runtime under the unversioned name libamdhip64.so.  If
+# libssw.so were loaded first, its libamdhip64.so.7 would come from /opt/rocm and torch would then
+# load a second HIP runtime into the process, whose device list the library's launches do not
+# share ("no ROCm-capable device").  Loaded after torch, libssw.so binds to torch's runtime (same
+# soname), so tensors, streams and events are all one runtime's objects.
+import torch  # noqa: F401  (import order matters, see above)
 
 __all__ = [
     "SSWError", "LIB_PATH", "sa_forward", "swa_forward", "gated_sa_swa_forward",

@@ -57,6 +57,11 @@ int check_forward(const char* who, const void* q, const void* k, const void* v, 
       ((int64_t)n * G / 128 + 1) * B * Hkv >= ((int64_t)1 << 31))
     return fail(SSW_ESHAPE, w + ": n * Hq / Hkv must be <= 2^31 - 4096, B * Hkv < 65536 and "
                                 "n * Hq * B / 128 < 2^31");
+  // K and V rows of one (batch row, KV head) are addressed with 32-bit byte offsets below 2^31
+  // (offset 2^31 is the kernels' "read zeros" marker)
+  const int64_t elem = dtype == SSW_BF16 ? 2 : 4;
+  if ((int64_t)n * Hkv * d * elem > ((int64_t)1 << 31) - 4096)
+    return fail(SSW_ESHAPE, w + ": n * Hkv * d * element size must be <= 2^31 - 4096 bytes");
   if (B == 0 || n == 0) return SSW_OK;
   if (!q || !k || !v || !out) return fail(SSW_EINVAL, w + ": q, k, v and out must be non-NULL");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))

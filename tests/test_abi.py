@@ -105,6 +105,7 @@ ALL_FWD = ["ssw_sa_forward", "ssw_swa_forward", "ssw_gated_sa_swa_forward",
     (dict(out=None), -1),
     (dict(Hq=6, Hkv=4), -2),
     (dict(n=2**30, Hq=8, Hkv=2), -2),
+    (dict(n=2**21, Hq=8, Hkv=8, d=128, dtype=0), -2),    # K/V rows past 2^31 bytes
     (dict(d=96), -3),
     (dict(d=256), -3),
     (dict(dtype=7), -3),
@@ -140,3 +141,19 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros(1, 8, 2, 64)
     with pytest.raises(TypeError):
         ssw.sa_forward(x, x[:, :, :1], x[:, :, :1], torch.arange(8, dtype=torch.int32), 4, True)
+
+
+def test_one_hip_runtime_in_process():
+    """Importing the binding must leave exactly one HIP runtime mapped (torch's).  A second copy,
+    pulled in when libssw.so is loaded before torch, makes every launch fail with "no ROCm-capable
+    device" on a GPU host."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import stochastic_sliding_window_amd, torch\n"
+        "maps = open('/proc/self/maps').read().splitlines()\n"
+        "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n" % ROOT)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip().splitlines()[-1] == "1"
