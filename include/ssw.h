@@ -52,7 +52,7 @@ typedef enum {
   SSW_OK = 0,
   SSW_EINVAL = -1,   /* window < 1, negative size, NULL required pointer, causal not 0/1 */
   SSW_ESHAPE = -2,   /* Hq not a multiple of Hkv, or sizes whose index range overflows:
-                        n * Hkv * d * element size must be <= 2^31 - 4096 bytes,
+                        n * Hq * d * element size must be <= 2^31 - 4096 bytes, n <= 2^24 - 64,
                         n * Hq / Hkv <= 2^31 - 4096 and B * Hkv < 65536 */
   SSW_EDTYPE = -3,   /* d not 64 or 128, or dtype not SSW_F32 / SSW_BF16 */
   SSW_EALIGN = -4,   /* q, k, v, out not 16-byte aligned; sigma, gates not 4-byte aligned */

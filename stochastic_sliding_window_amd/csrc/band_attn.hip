@@ -57,6 +57,12 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 #ifndef SSW_STAGES
 #define SSW_STAGES 4
 #endif
+#ifndef SSW_WPE
+#define SSW_WPE 2  // waves per SIMD the register allocation is sized for
+#endif
+#ifndef SSW_PIPELINE
+#define SSW_PIPELINE 1  // scores of chunk c + 1 computed alongside the softmax of chunk c
+#endif
 #ifndef SSW_XCD_REMAP
 #define SSW_XCD_REMAP 1
 #endif
@@ -67,7 +73,10 @@ constexpr int kColsWave = 32;
 constexpr int kColsWG = kColsWave * kWaves;
 constexpr int kChunk = 32;
 constexpr int kStages = SSW_STAGES;  // LDS ring depth: kStages - 1 chunks in flight
-constexpr int kSigCap = 2048;  // sigma entries held in LDS at a time (64 chunks)
+#ifndef SSW_SIGCAP
+#define SSW_SIGCAP 2048
+#endif
+constexpr int kSigCap = SSW_SIGCAP;  // sigma entries held in LDS at a time
 constexpr int kSegChunks = kSigCap / kChunk;
 constexpr float kLazy = 8.0f;  // reference max may lag the true max by up to 2^8 (log2 units)
 // bf16 gated path: the SWA pass leaves g_swa * Y_swa in the output buffer as fp16 scaled by 2^-8
@@ -233,7 +242,7 @@ __device__ __forceinline__ int xcd_local_order(int i, int nblocks) {
 }
 
 template <typename T, int D, bool PERM, bool SIGMASK, int EPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SSW_WPE, SSW_WPE)))
 void band_attn_kernel(Params prm) {
   using Lay = Layout<T, D>;
   constexpr bool kBf16 = Lay::kBf16;
@@ -326,6 +335,9 @@ void band_attn_kernel(Params prm) {
     }
     return r;
   };
+  // Row offsets are one 24-bit multiply-add (rows <= n < 2^24 - 32 and the row stride < 2^24 are
+  // checked at the API).  Keys past the sequence end need no test: their row is >= n (the key
+  // itself, or the sigma entry patched to n), which lies past the buffer range and reads zeros.
   auto dma_issue = [&](int kc0, auto stage_c, const DmaRows& r) {
     constexpr int STAGE = decltype(stage_c)::value;
 #pragma unroll
@@ -333,12 +345,44 @@ void band_attn_kernel(Params prm) {
       const int I = wave * kDW + i;  // wave-uniform
       const bool isv = I >= Lay::kDmaK;
       const int blkid = isv ? I - Lay::kDmaK : I;
-      const int q = kc0 + dma_key[i];
-      const uint32_t voff =
-          q < n ? (uint32_t)r.row[i] * row_stride32 + dma_goff[i] : kOutOfRange;
+      const uint32_t voff = __umul24((uint32_t)r.row[i], row_stride32) + dma_goff[i];
       const uint32_t lds = smem_lds + STAGE * Lay::kStageBytes + (isv ? Lay::kMatBytes : 0) +
                            blkid * 1024;
       dma16(isv ? rs_v : rs_k, __builtin_amdgcn_readfirstlane(lds), voff);
+    }
+  };
+  // Gated SA pass (bf16): the intermediate rows this wave will add to are fetched into LDS while
+  // its last chunk is processed.  Only that chunk's stage is still in use then, so waves 2j and
+  // 2j + 1 take the two halves of the stage STAGE + 1 + j.  Instruction i brings the rows of the
+  // wave's columns i * (1024 / RB) ..., lane l granule l % kGran of column i * (1024 / RB) +
+  // l / kGran; granules are XOR-swizzled by column so the epilogue's reads spread over banks.
+  constexpr bool kPrefetchPartial = EPI == kEpiAddPartial && kBf16;
+  const int64_t out_batch_bytes = (int64_t)n * prm.Hq * D * (int)sizeof(T);
+  const i32x4 rs_out =
+      make_rsrc(prm.out + (int64_t)b * out_batch_bytes, (uint32_t)out_batch_bytes);
+  auto partial_region = [&](int last_stage) {
+    return ((last_stage + 1 + wave / 2) % Lay::kNS) * Lay::kStageBytes +
+           (wave % 2) * Lay::kMatBytes;
+  };
+  auto dma_partial = [&](int last_stage, uint32_t my_out_off) {
+    const uint32_t region = smem_lds + partial_region(last_stage);
+    constexpr int kColsPerDma = 1024 / Lay::kRowBytes;
+#pragma unroll
+    for (int i = 0; i < Lay::kDmaK; ++i) {
+      const int c = i * kColsPerDma + lane / Lay::kGran;  // wave-relative column
+      const uint32_t base = (uint32_t)__builtin_amdgcn_ds_bpermute(c * 4, (int)my_out_off);
+      const int gran = (lane % Lay::kGran) ^ (c & (Lay::kGran - 1));
+      dma16(rs_out, __builtin_amdgcn_readfirstlane(region + 1024 * i), base + 16 * gran);
+    }
+  };
+  // After a sigma segment has landed (and a barrier): the entries of keys past the sequence end
+  // (read as 0 by the buffer range check) become n, so their K/V rows fall outside the buffers.
+  // Only a segment that crosses the end does this, with one more barrier.
+  auto patch_sigma_tail = [&](int seg_key0, int nseg_chunks) {
+    const int key_end = seg_key0 + nseg_chunks * kChunk;
+    if (key_end > n) {
+      for (int key = n + tid; key < key_end; key += kThreads) sig_lds[key - seg_key0] = n;
+      __syncthreads();
     }
   };
   auto dma_chunk = [&](int kc0, auto stage_c, int seg_key0) {
@@ -354,12 +398,19 @@ void band_attn_kernel(Params prm) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (PERM) patch_sigma_tail(kbeg, min(nchunks, kSegChunks));
   // the first chunks of the first segment go in flight before Q is loaded, so the two overlap
   static_for<Lay::kPF>([&](auto pf) {
     if (pf() < min(nchunks, kSegChunks)) dma_chunk(kbeg + pf() * kChunk, pf, kbeg);
   });
 
   const int64_t qrow_elems = (((int64_t)b * n + myorig) * prm.Hq + h) * D;
+  // the gate is fetched now, with Q, instead of in the epilogue
+  const float gate_v = prm.gate ? prm.gate[((int64_t)b * n + myorig) * prm.Hq + h] : 1.0f;
+  // byte offset of this column's output row within batch row b (the out buffer holds
+  // n * Hq * D elements per batch row, < 2^31 bytes as checked at the API)
+  const uint32_t out_off =
+      colvalid ? (uint32_t)(((int64_t)myorig * prm.Hq + h) * (D * (int)sizeof(T))) : kOutOfRange;
   constexpr int kQRegs = kBf16 ? D / 16 : D / 2;
   typedef typename std::conditional<kBf16, bf16x8, float>::type QFrag;
   QFrag qf[kQRegs];
@@ -446,16 +497,23 @@ void band_attn_kernel(Params prm) {
     return s;
   };
 
-  // mask, online softmax and O^T += V^T P^T for chunk c (ring slot STAGE) given its scores
-  auto softmax_pv = [&](int c, auto stage_c, int seg_key0, const f32x16& s) {
+  // A chunk is interior for this wave when every key of it lies inside the band of every one of
+  // the wave's slots (and before the sequence end): then only the causal sigma test remains.
+  auto is_interior = [&](int c) {
+    const int kc0 = kbeg + c * kChunk;
+    return kc0 >= w_shi - L && kc0 + kChunk - 1 <= w_slo + R && kc0 + kChunk - 1 < n;
+  };
+
+  // Mask, online softmax and O^T += V^T P^T for chunk c (ring slot STAGE) given its scores.
+  // INTERIOR selects the mask form (is_interior(c) must agree).
+  auto softmax_pv = [&](int c, auto stage_c, auto interior_c, int seg_key0, const f32x16& s) {
     constexpr int STAGE = decltype(stage_c)::value;
+    constexpr bool INTERIOR = decltype(interior_c)::value;
     const int kc0 = kbeg + c * kChunk;
     const char* Kst = smem + STAGE * Lay::kStageBytes;
     const char* Vst = Kst + Lay::kMatBytes;
 
     // mask.  Register r holds key kc0 + 16(r/8) + 8*h32 + r%8.
-    const bool interior =
-        kc0 >= w_shi - L && kc0 + kChunk - 1 <= w_slo + R && kc0 + kChunk - 1 < n;
     int sk[16];
     if constexpr (SIGMASK) {
       const int* sp = sig_lds + (kc0 - seg_key0);
@@ -474,7 +532,7 @@ void band_attn_kernel(Params prm) {
     // interior chunks need only the causal test; edge chunks also test the lane's band, held as a
     // bit mask over the chunk's 32 key offsets.
     float sm[16];
-    if (interior) {
+    if constexpr (INTERIOR) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         bool ok = true;
@@ -501,6 +559,9 @@ void band_attn_kernel(Params prm) {
     const float mx = mraw * prm.scale_log2;  // log2 units
 
     const bool need = mx > m_ref + kLazy;
+    // O is still exactly zero while the reference is -inf (every earlier key was masked), so the
+    // first raise of the reference needs no rescale
+    const bool rescale = need && m_ref != -INFINITY;
     const float m_new = need ? mx : m_ref;
     const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
     m_ref = m_new;
@@ -509,7 +570,7 @@ void band_attn_kernel(Params prm) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[r], prm.scale_log2, -m_use));
-    if (__ballot(need)) {
+    if (__ballot(rescale)) {
 #pragma unroll
       for (int t = 0; t < kOT; ++t) o[t] *= alpha;
     }
@@ -569,6 +630,126 @@ void band_attn_kernel(Params prm) {
     }
   };
 
+  // bf16: softmax and P*V of chunk c (ring slot STAGE) fused with the scores of the next chunk
+  // (ring slot NEXT), which are returned.  The next chunk's MFMAs do not depend on this chunk's
+  // softmax, so they are issued inside the straight-line stretch between the mask and the lazy
+  // rescale branch, where the scheduler can interleave them with the column max and the first
+  // half of the exponentials.  Every step's arithmetic is that of compute_s and softmax_pv.
+  // The mask form is a runtime (uniform) branch that only produces sm[], so O keeps one set of
+  // registers on every path.
+  auto fused_step = [&](int c, auto stage_c, auto next_c, bool interior, int seg_key0,
+                        const f32x16& s) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    constexpr int NEXT = decltype(next_c)::value;
+    f32x16 sn = zero16();
+    if constexpr (kBf16) {
+      const int kc0 = kbeg + c * kChunk;
+      const char* Kst = smem + STAGE * Lay::kStageBytes;
+      const char* Kn = smem + (NEXT >= 0 ? NEXT : 0) * Lay::kStageBytes;
+
+      // mask.  Register r holds key kc0 + 16(r/8) + 8*h32 + r%8.
+      int sk[16];
+      if constexpr (SIGMASK) {
+        const int* sp = sig_lds + (kc0 - seg_key0);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const u32x4 a = *(const u32x4*)(sp + 16 * half + 8 * h32);
+          const u32x4 bq = *(const u32x4*)(sp + 16 * half + 8 * h32 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sk[8 * half + e] = (int)a[e];
+            sk[8 * half + 4 + e] = (int)bq[e];
+          }
+        }
+      }
+      float sm[16];
+      if (interior) {
+        // all compares first (each into its own lane mask), then the selects: no compare is
+        // followed directly by the select that reads its mask
+        bool ok[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          ok[r] = true;
+          if constexpr (SIGMASK) ok[r] = sk[r] <= myorig;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm[r] = ok[r] ? s[r] : -INFINITY;
+      } else {
+        const int a = max(max(myslot - L, 0) - kc0, 0);
+        const int z = min(min(myslot + R, n - 1) - kc0, 31);
+        const uint32_t upto = z < 0 ? 0u : (0xFFFFFFFFu >> (31 - z));
+        const uint32_t from = a > 31 ? 0u : (0xFFFFFFFFu << a);
+        const uint32_t bm = (upto & from) >> (8 * h32);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          bool ok = (bm >> (16 * (r >> 3) + (r & 7))) & 1u;
+          if constexpr (SIGMASK) ok = ok & (sk[r] <= myorig);
+          sm[r] = ok ? s[r] : -INFINITY;
+        }
+      }
+
+      // scores of the next chunk, interleaved with the column max and the first weights
+      if constexpr (NEXT >= 0) {
+#pragma unroll
+        for (int kb = 0; kb < D / 16; ++kb) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kn + k_off[kb]));
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], sn, 0, 0, 0);
+        }
+      }
+      float mraw = sm[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mraw = fmaxf(mraw, sm[r]);
+      mraw = pair_max(mraw);
+      const float mx = mraw * prm.scale_log2;
+      const bool need = mx > m_ref + kLazy;
+      // O is still exactly zero while the reference is -inf (every earlier key was masked), so
+      // the first raise of the reference needs no rescale
+      const bool rescale = need && m_ref != -INFINITY;
+      const float m_new = need ? mx : m_ref;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+      m_ref = m_new;
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[r], prm.scale_log2, -m_use));
+      bf16x8 pb[2];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[0][e] = (__bf16)p[e];
+        pb[1][e] = (__bf16)p[8 + e];
+      }
+      if (__ballot(rescale)) {
+#pragma unroll
+        for (int t = 0; t < kOT; ++t) o[t] *= alpha;
+      }
+      float psum = 0.f;
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0][e], pb[0][e + 1]}, one2, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][e], pb[1][e + 1]}, one2, psum, false);
+      }
+      l_run = l_run * alpha + psum;
+      const SSW_LDS char* vbase = (const SSW_LDS char*)Kst;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int db = 0; db < kOT; ++db) {
+          const SSW_LDS char* vp = vbase + v_off[db] + 16 * t * Lay::kRowBytes;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)vp);
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)(vp + 4 * Lay::kRowBytes));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+          const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], o[db], 0, 0, 0);
+        }
+      }
+    }
+    return sn;
+  };
+
   // ---- main loop over segments of at most kSegChunks chunks (one segment in practice)
   for (int sg = 0; sg < nseg; ++sg) {
     const int c0 = sg * kSegChunks;
@@ -582,12 +763,14 @@ void band_attn_kernel(Params prm) {
         dma_sigma(seg_key0, segc);
         wait_vmcnt<0>();
         __syncthreads();
+        patch_sigma_tail(seg_key0, segc);
       }
       static_for<Lay::kPF>([&](auto pf) {
         if (pf() < segc) dma_chunk(seg_key0 + pf() * kChunk, pf, seg_key0);
       });
     }
 
+#if SSW_PIPELINE
     // Software pipeline: while chunk cs is consumed (softmax + P*V from its V), the scores of
     // chunk cs + 1 are already computed from its K, so each wave has independent MFMA work to
     // overlap with the softmax VALU work.  Chunk cs + kPF is fetched meanwhile.
@@ -620,22 +803,88 @@ void band_attn_kernel(Params prm) {
           if (fetch)
             dma_issue(seg_key0 + (cs + Lay::kPF) * kChunk, std::integral_constant<int, kFetch>{},
                       rows);
+          if constexpr (kPrefetchPartial)
+            if (sg == nseg - 1 && cs == segc - 1 && wave_on) dma_partial(u(), out_off);
+          // bf16: one code path for every chunk a wave touches (a chunk outside the wave's band is
+          // fully masked by the edge form and adds nothing; the scores computed past the last
+          // chunk are discarded).  fp32: scores and softmax as separate steps.
+          const bool act_cur = active(c0 + cs);
+          const bool act_next = cs + 1 < segc && active(c0 + cs + 1);
+          using Next = std::integral_constant<int, kNext>;
+          using Edge = std::false_type;
+          using Inner = std::true_type;
           f32x16 s_next = zero16();
-          if (cs + 1 < segc && active(c0 + cs + 1))
-            s_next = compute_s(std::integral_constant<int, kNext>{});
-          if (active(c0 + cs)) softmax_pv(c0 + cs, u, seg_key0, s_cur);
+          if constexpr (kBf16) {
+            if (act_cur || act_next)
+              s_next = fused_step(c0 + cs, u, Next{}, is_interior(c0 + cs), seg_key0, s_cur);
+          } else {
+            if (act_next) s_next = compute_s(Next{});
+            if (act_cur) {
+              if (is_interior(c0 + cs))
+                softmax_pv(c0 + cs, u, Inner{}, seg_key0, s_cur);
+              else
+                softmax_pv(c0 + cs, u, Edge{}, seg_key0, s_cur);
+            }
+          }
           s_cur = s_next;
         }
       });
     }
   }
+#else
+    // Chunk cs is consumed in iteration cs (scores, softmax, P*V) while chunks cs + 1 .. cs + kPF
+    // are in flight; the fetch of chunk cs + kPF reuses the slot of chunk cs - 1.
+    auto active = [&](int c) { return wave_on && c >= c_first && c <= c_last; };
+    // unrolled by the ring depth so that every chunk's ring slot is a compile-time constant
+    for (int cs0 = 0; cs0 < segc; cs0 += Lay::kNS) {
+      static_for<Lay::kNS>([&](auto u) {
+        const int cs = cs0 + u();
+        if (cs < segc) {
+          constexpr int kFetch = (u() + Lay::kPF) % Lay::kNS;
+          const bool fetch = cs + Lay::kPF < segc;
+          DmaRows rows;
+          if (fetch) rows = dma_prep(seg_key0 + (cs + Lay::kPF) * kChunk, seg_key0);
+          // chunk cs must have landed: at most kPF - 1 younger chunks of this wave's DMAs may
+          // still be outstanding; near the end, wait for everything
+          if (cs + Lay::kPF - 1 < segc)
+            wait_vmcnt<Lay::kDmaPerWave * (Lay::kPF - 1)>();
+          else
+            wait_vmcnt<0>();
+          __syncthreads();  // every wave's DMAs for chunk cs landed; chunk cs - 1 consumed
+          if (fetch)
+            dma_issue(seg_key0 + (cs + Lay::kPF) * kChunk, std::integral_constant<int, kFetch>{},
+                      rows);
+          if constexpr (kPrefetchPartial)
+            if (sg == nseg - 1 && cs == segc - 1 && wave_on) dma_partial(u(), out_off);
+          if (active(c0 + cs)) {
+            const f32x16 sc = compute_s(u);
+            if constexpr (kBf16) {
+              fused_step(c0 + cs, u, std::integral_constant<int, -1>{}, is_interior(c0 + cs),
+                         seg_key0, sc);
+            } else {
+              if (is_interior(c0 + cs))
+                softmax_pv(c0 + cs, u, std::true_type{}, seg_key0, sc);
+              else
+                softmax_pv(c0 + cs, u, std::false_type{}, seg_key0, sc);
+            }
+          }
+        }
+      });
+    }
+  }
+#endif
 
   // ---- epilogue: normalise, gate, scatter to original row sigma[p]
   const float l_tot = pair_sum(l_run);
   if (!colvalid) return;
-  float f = 1.0f / l_tot;
-  if (prm.gate) f *= prm.gate[((int64_t)b * n + myorig) * prm.Hq + h];
+  const float f = __builtin_amdgcn_rcpf(l_tot) * gate_v;
   char* orow = prm.out + qrow_elems * (int64_t)sizeof(T);
+  const char* prow = nullptr;  // this column's prefetched intermediate row (LDS)
+  if constexpr (kPrefetchPartial) {
+    wait_vmcnt<0>();
+    const int segc_last = nchunks - (nseg - 1) * kSegChunks;
+    prow = smem + partial_region((segc_last - 1) % Lay::kNS) + (lane & 31) * Lay::kRowBytes;
+  }
 #pragma unroll
   for (int t = 0; t < kOT; ++t) {
 #pragma unroll
@@ -659,7 +908,9 @@ void band_attn_kernel(Params prm) {
           *dst = u32x2{w[0], w[1]};
         } else {
           if constexpr (EPI == kEpiAddPartial) {
-            const u32x2 old = *dst;
+            // granule d0 / 8 of the row, swizzled by column; bytes 8 * h32 within it
+            const int gsw = ((d0 >> 3) ^ ((lane & 31) & (Lay::kGran - 1)));
+            const u32x2 old = *(const u32x2*)(prow + 16 * gsw + 8 * h32);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
               y[2 * u] += (float)__builtin_bit_cast(_Float16, (uint16_t)(old[u] & 0xffffu)) *

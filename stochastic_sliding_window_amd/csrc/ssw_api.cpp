@@ -59,9 +59,15 @@ int check_forward(const char* who, const void* q, const void* k, const void* v, 
                                 "n * Hq * B / 128 < 2^31");
   // K and V rows of one (batch row, KV head) are addressed with 32-bit byte offsets below 2^31
   // (offset 2^31 is the kernels' "read zeros" marker)
+  // (and row offsets are formed with 24-bit multiplies: n <= 2^24 - 64, a K/V token row < 2^24
+  // bytes);
+  // one batch row of out is addressed the same way
   const int64_t elem = dtype == SSW_BF16 ? 2 : 4;
-  if ((int64_t)n * Hkv * d * elem > ((int64_t)1 << 31) - 4096)
-    return fail(SSW_ESHAPE, w + ": n * Hkv * d * element size must be <= 2^31 - 4096 bytes");
+  if ((int64_t)n * Hkv * d * elem > ((int64_t)1 << 31) - 4096 ||
+      (int64_t)n * Hq * d * elem > ((int64_t)1 << 31) - 4096 || n > (1 << 24) - 64 ||
+      (int64_t)Hkv * d * elem >= (1 << 24))
+    return fail(SSW_ESHAPE, w + ": n * Hq * d * element size must be <= 2^31 - 4096 bytes and "
+                                "n <= 2^24 - 64");
   if (B == 0 || n == 0) return SSW_OK;
   if (!q || !k || !v || !out) return fail(SSW_EINVAL, w + ": q, k, v and out must be non-NULL");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
