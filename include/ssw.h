@@ -96,14 +96,17 @@ int ssw_gated_sa_swa_forward(const void* q, const void* k, const void* v, const 
                              int window, int causal, const float* gates, void* out,
                              int B, int n, int Hq, int Hkv, int d, int dtype, void* stream);
 
-/* Same as ssw_gated_sa_swa_forward, and additionally records the given HIP events (hipEvent_t,
- * each may be NULL) on `stream` before the SWA pass, between the passes and after the SA pass, so
- * a caller can time each kernel.  Events must have been created by the caller. */
+/* Same as ssw_gated_sa_swa_forward, and additionally times each of its two kernels: the given
+ * HIP events (hipEvent_t created by the caller; each may be NULL) are attached to the kernels'
+ * dispatches, so ev_swa_start / ev_swa_end are recorded when the SWA pass starts and ends and
+ * ev_sa_start / ev_sa_end likewise for the SA pass.  No separate event packets are queued, so the
+ * calls run back to back as in the untimed form and hipEventElapsedTime gives each kernel's own
+ * duration. */
 int ssw_gated_sa_swa_forward_timed(const void* q, const void* k, const void* v,
                                    const int32_t* sigma, int window, int causal,
                                    const float* gates, void* out, int B, int n, int Hq, int Hkv,
-                                   int d, int dtype, void* stream, void* ev_start,
-                                   void* ev_between, void* ev_end);
+                                   int d, int dtype, void* stream, void* ev_swa_start,
+                                   void* ev_swa_end, void* ev_sa_start, void* ev_sa_end);
 
 /* Host helpers (HOST pointers, no GPU needed). */
 

@@ -70,7 +70,7 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = fwd
         fn.restype = ctypes.c_int
-    lib.ssw_gated_sa_swa_forward_timed.argtypes = fwd + [vp, vp, vp]
+    lib.ssw_gated_sa_swa_forward_timed.argtypes = fwd + [vp, vp, vp, vp]
     lib.ssw_gated_sa_swa_forward_timed.restype = ctypes.c_int
     lib.ssw_make_permutation.argtypes = [ctypes.c_uint64, i32, i32p, i32p]
     lib.ssw_make_permutation.restype = ctypes.c_int
@@ -220,9 +220,9 @@ def swa_forward(q, k, v, window: int, causal: bool, gate=None, out=None):
 def gated_sa_swa_forward(q, k, v, sigma, window: int, causal: bool, gates, out=None, events=None):
     """Y = g_sa * SA + g_swa * SWA with gates [2, B, n, Hq] (ssw_gated_sa_swa_forward).
 
-    ``events``: optional (start, between, end) torch.cuda.Event triple recorded around the two
-    kernels (ssw_gated_sa_swa_forward_timed); each must have been recorded once already so that
-    its HIP event exists.
+    ``events``: optional (swa_start, swa_end, sa_start, sa_end) torch.cuda.Event 4-tuple attached
+    to the two kernels' dispatches (ssw_gated_sa_swa_forward_timed); each must have been recorded
+    once already so that its HIP event exists.
     """
     out = _prep(q, k, v, out)
     B, n, Hq, d = q.shape
@@ -236,6 +236,8 @@ def gated_sa_swa_forward(q, k, v, sigma, window: int, causal: bool, gates, out=N
     if events is None:
         _check(_lib.ssw_gated_sa_swa_forward(*args))
     else:
+        if len(events) != 4:
+            raise ValueError("events: (swa_start, swa_end, sa_start, sa_end)")
         handles = []
         for e in events:
             if e is None:

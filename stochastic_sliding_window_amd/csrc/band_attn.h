@@ -31,6 +31,10 @@ struct BandLaunch {
   bool causal;
   bool perm;
   int epilogue;          // Epilogue
+  // optional hipEvent_t pair attached to the kernel's dispatch: recorded when the kernel starts
+  // and when it ends (no separate event packets around it)
+  void* ev_start = nullptr;
+  void* ev_stop = nullptr;
 };
 
 hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream);

@@ -31,6 +31,7 @@
 //     Masks are evaluated per element only where a chunk touches the band edge or when the causal
 //     rule needs sigma.
 //   * Epilogue: divide by the row sum, multiply by the gate, scatter to row sigma[p].
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -960,25 +961,33 @@ __global__ void neighbor_mask_kernel(const int32_t* sigma, int n, int L, int R, 
 
 // ---- host-side dispatch
 template <typename T, int D, bool PERM, bool SIGMASK, int EPI>
-static hipError_t launch_t(const Params& prm, hipStream_t stream) {
-  hipLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, EPI>), dim3(prm.nblocks),
-                     dim3(kThreads), 0, stream, prm);
+static hipError_t launch_t(const Params& prm, hipStream_t stream, void* ev_start, void* ev_stop) {
+  if (ev_start || ev_stop) {
+    hipExtLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, EPI>), dim3(prm.nblocks),
+                          dim3(kThreads), 0, stream, (hipEvent_t)ev_start, (hipEvent_t)ev_stop, 0,
+                          prm);
+  } else {
+    hipLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, EPI>), dim3(prm.nblocks),
+                       dim3(kThreads), 0, stream, prm);
+  }
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_d(const BandLaunch& a, const Params& prm, hipStream_t s) {
+  void* e0 = a.ev_start;
+  void* e1 = a.ev_stop;
   // The SA pass of the gated path adds to the SWA pass's intermediate; nothing else combines.
   if (a.perm) {
     const bool add = a.epilogue == kEpiAddPartial;
     if (a.causal)
-      return add ? launch_t<T, D, true, true, kEpiAddPartial>(prm, s)
-                 : launch_t<T, D, true, true, kEpiStore>(prm, s);
-    return add ? launch_t<T, D, true, false, kEpiAddPartial>(prm, s)
-               : launch_t<T, D, true, false, kEpiStore>(prm, s);
+      return add ? launch_t<T, D, true, true, kEpiAddPartial>(prm, s, e0, e1)
+                 : launch_t<T, D, true, true, kEpiStore>(prm, s, e0, e1);
+    return add ? launch_t<T, D, true, false, kEpiAddPartial>(prm, s, e0, e1)
+               : launch_t<T, D, true, false, kEpiStore>(prm, s, e0, e1);
   }
-  return a.epilogue == kEpiPartial ? launch_t<T, D, false, false, kEpiPartial>(prm, s)
-                                   : launch_t<T, D, false, false, kEpiStore>(prm, s);
+  return a.epilogue == kEpiPartial ? launch_t<T, D, false, false, kEpiPartial>(prm, s, e0, e1)
+                                   : launch_t<T, D, false, false, kEpiStore>(prm, s, e0, e1);
 }
 
 hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream) {

@@ -160,8 +160,8 @@ int ssw_swa_forward(const void* q, const void* k, const void* v, const int32_t* 
 
 static int gated(const char* who, const void* q, const void* k, const void* v,
                  const int32_t* sigma, int window, int causal, const float* gates, void* out,
-                 int B, int n, int Hq, int Hkv, int d, int dtype, void* stream, void* ev_start,
-                 void* ev_between, void* ev_end) {
+                 int B, int n, int Hq, int Hkv, int d, int dtype, void* stream,
+                 void* const* events) {
   int st = check_forward(who, q, k, v, out, window, causal, B, n, Hq, Hkv, d, dtype);
   if (st != SSW_OK || B == 0 || n == 0) return st;
   if (!sigma || !gates) return fail(SSW_EINVAL, std::string(who) + ": sigma and gates must be non-NULL");
@@ -172,13 +172,6 @@ static int gated(const char* who, const void* q, const void* k, const void* v,
     st = check_sigma_on_device(sigma, n, s);
     if (st != SSW_OK) return st;
   }
-  auto mark = [&](void* ev) -> int {
-    if (!ev) return SSW_OK;
-    hipError_t e = hipEventRecord((hipEvent_t)ev, s);
-    if (e != hipSuccess)
-      return fail(SSW_EHIP, std::string(who) + ": hipEventRecord failed: " + hipGetErrorString(e));
-    return SSW_OK;
-  };
   const float* g_sa = gates;
   const float* g_swa = gates + (size_t)B * n * Hq;
   // Pass 1: the SWA pass leaves g_swa * Y_swa in `out` as the intermediate (fp32, or for bf16
@@ -192,27 +185,31 @@ static int gated(const char* who, const void* q, const void* k, const void* v,
   ssw::BandLaunch a2 =
       make_launch(q, k, v, sigma, window, causal, g_sa, out, B, n, Hq, Hkv, d, dtype);
   a2.epilogue = ssw::kEpiAddPartial;
-  if ((st = mark(ev_start)) != SSW_OK) return st;
+  if (events) {
+    a1.ev_start = events[0];
+    a1.ev_stop = events[1];
+    a2.ev_start = events[2];
+    a2.ev_stop = events[3];
+  }
   if ((st = run(who, a1, s)) != SSW_OK) return st;
-  if ((st = mark(ev_between)) != SSW_OK) return st;
-  if ((st = run(who, a2, s)) != SSW_OK) return st;
-  return mark(ev_end);
+  return run(who, a2, s);
 }
 
 int ssw_gated_sa_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma,
                              int window, int causal, const float* gates, void* out, int B, int n,
                              int Hq, int Hkv, int d, int dtype, void* stream) {
   return gated("ssw_gated_sa_swa_forward", q, k, v, sigma, window, causal, gates, out, B, n, Hq,
-               Hkv, d, dtype, stream, nullptr, nullptr, nullptr);
+               Hkv, d, dtype, stream, nullptr);
 }
 
 int ssw_gated_sa_swa_forward_timed(const void* q, const void* k, const void* v,
                                    const int32_t* sigma, int window, int causal,
                                    const float* gates, void* out, int B, int n, int Hq, int Hkv,
-                                   int d, int dtype, void* stream, void* ev_start,
-                                   void* ev_between, void* ev_end) {
+                                   int d, int dtype, void* stream, void* ev_swa_start,
+                                   void* ev_swa_end, void* ev_sa_start, void* ev_sa_end) {
+  void* const events[4] = {ev_swa_start, ev_swa_end, ev_sa_start, ev_sa_end};
   return gated("ssw_gated_sa_swa_forward_timed", q, k, v, sigma, window, causal, gates, out, B,
-               n, Hq, Hkv, d, dtype, stream, ev_start, ev_between, ev_end);
+               n, Hq, Hkv, d, dtype, stream, events);
 }
 
 int ssw_make_permutation(uint64_t seed, int n, int32_t* sigma_out, int32_t* inv_out) {

@@ -72,7 +72,7 @@ _FWD_ARGS = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 2 + [ctypes.c_void_p] * 2 +
 for _n in ("ssw_sa_forward", "ssw_swa_forward", "ssw_gated_sa_swa_forward"):
     getattr(_lib, _n).argtypes = _FWD_ARGS
     getattr(_lib, _n).restype = ctypes.c_int
-_lib.ssw_gated_sa_swa_forward_timed.argtypes = _FWD_ARGS + [ctypes.c_void_p] * 3
+_lib.ssw_gated_sa_swa_forward_timed.argtypes = _FWD_ARGS + [ctypes.c_void_p] * 4
 _lib.ssw_gated_sa_swa_forward_timed.restype = ctypes.c_int
 _lib.ssw_last_error.restype = ctypes.c_char_p
 
@@ -84,7 +84,7 @@ GOOD = dict(q=P, k=P, v=P, sigma=P, window=8, causal=1, gate=None, out=P,
 def _call(fn, **kw):
     a = dict(GOOD)
     a.update(kw)
-    extra = (None, None, None) if fn.endswith("_timed") else ()
+    extra = (None, None, None, None) if fn.endswith("_timed") else ()
     return getattr(_lib, fn)(a["q"], a["k"], a["v"], a["sigma"], a["window"], a["causal"],
                              a["gate"], a["out"], a["B"], a["n"], a["Hq"], a["Hkv"], a["d"],
                              a["dtype"], None, *extra)

@@ -190,14 +190,16 @@ def test_timed_gated_call_matches_untimed():
     _, dev = _data(21, B, n, Hq, Hkv, d, "bf16")
     sig_dev, _ = _sigma(22, n)
     q, k, v, g = dev
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     for e in evs:
         e.record()
     a = ssw.gated_sa_swa_forward(q, k, v, sig_dev, w, True, g)
     b = ssw.gated_sa_swa_forward(q, k, v, sig_dev, w, True, g, events=evs)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
-    assert evs[0].elapsed_time(evs[1]) > 0 and evs[1].elapsed_time(evs[2]) > 0
+    # each pair brackets one kernel; the SA pass starts no earlier than the SWA pass ends
+    assert evs[0].elapsed_time(evs[1]) > 0 and evs[2].elapsed_time(evs[3]) > 0
+    assert evs[1].elapsed_time(evs[2]) >= 0
 
 
 def test_empty_inputs_are_noops():
