@@ -357,7 +357,9 @@ void band_attn_kernel(Params prm) {
   // 2j + 1 take the two halves of the stage STAGE + 1 + j.  Instruction i brings the rows of the
   // wave's columns i * (1024 / RB) ..., lane l granule l % kGran of column i * (1024 / RB) +
   // l / kGran; granules are XOR-swizzled by column so the epilogue's reads spread over banks.
-  constexpr bool kPrefetchPartial = EPI == kEpiAddPartial && kBf16;
+  // (needs kWaves / 2 ring stages besides the last chunk's)
+  constexpr bool kPrefetchPartial =
+      EPI == kEpiAddPartial && kBf16 && Lay::kNS - 1 >= (kWaves + 1) / 2;
   const int64_t out_batch_bytes = (int64_t)n * prm.Hq * D * (int)sizeof(T);
   const i32x4 rs_out =
       make_rsrc(prm.out + (int64_t)b * out_batch_bytes, (uint32_t)out_batch_bytes);
