@@ -1,6 +1,7 @@
 """Benchmark: gated SA+SWA forward on one MI355X, long-context layer n = 32768, w = 128.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu-baseline]
+    python bench.py --nsweep      (SA against full causal attention, n = 2K .. 32K)
 
 One step is one pass of the whole hot path over one layer's synthetic input: one call of
 ssw_gated_sa_swa_forward, i.e. the SWA pass (leaves g_swa * Y_swa as the intermediate) followed by
@@ -64,6 +65,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time SA / SWA alone at w 32, 64, 128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size (0 = auto)")
+    ap.add_argument("--nsweep", action="store_true",
+                    help="instead: SA (w = --window) against full causal attention for n = 2K..32K")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -76,6 +79,9 @@ def main():
 
     import stochastic_sliding_window_amd as ssw
     import synth
+
+    if args.nsweep:
+        return nsweep(args)
 
     wl = synth.workload(4)
     B, n, Hq, Hkv, d = wl.B, wl.n, wl.Hq, wl.Hkv, wl.d
@@ -205,6 +211,62 @@ def main():
     }
     if sweep:
         line["sweep_us"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+def nsweep(args):
+    """SA (causal, w = --window) against full causal attention on the same kernels (the SWA kernel
+    with a window covering the sequence), layer shape of the long-context workload (32 query / 8 KV
+    heads, d 128, bf16), n = 2048 .. 32768.  Prints one JSON line with per-n times and the ratio."""
+    import numpy as np
+    import torch
+
+    import stochastic_sliding_window_amd as ssw
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    w = args.window
+    B, Hq, Hkv, d = 1, 32, 8, 128
+    rows = []
+    for n in (2048, 4096, 8192, 16384, 32768):
+        q, k, v = synth.qkv(synth.data_seed(4, 0), B, n, Hq, Hkv, d, "bf16")
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        sigma = torch.from_numpy(ssw.make_permutation(synth.sigma_seed(4, 0), n)).to(dev)
+        out = torch.empty_like(q)
+
+        def timed(fn, reps):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            start.record(stream)
+            for _ in range(reps):
+                fn()
+            end.record(stream)
+            torch.cuda.synchronize()
+            return start.elapsed_time(end) / reps
+
+        t_sa = timed(lambda: ssw.sa_forward(q, k, v, sigma, w, True, out=out), 20)
+        t_full = timed(lambda: ssw.swa_forward(q, k, v, n, True, out=out), 3 if n >= 16384 else 10)
+        full_flops = 4 * d * B * Hq * (n * (n + 1) // 2)
+        sa_flops = 4 * d * B * Hq * causal_pairs(n, w)
+        row = {"n": n, "sa_us": round(t_sa * 1e3, 1), "full_us": round(t_full * 1e3, 1),
+               "full_over_sa": round(t_full / t_sa, 2),
+               "sa_tflops": round(sa_flops / (t_sa * 1e-3) / 1e12, 1),
+               "full_tflops": round(full_flops / (t_full * 1e-3) / 1e12, 1)}
+        log(f"n={n}: SA w={w} {row['sa_us']} us, full causal {row['full_us']} us, "
+            f"ratio {row['full_over_sa']}x; full attention {row['full_tflops']} TFLOP/s "
+            f"({row['full_tflops'] / BF16_PEAK_TFLOPS:.1%} of bf16 MFMA peak)")
+        rows.append(row)
+        del q, k, v, out
+    line = {"metric": "full causal attention time / SA time (same kernels), 1 GPU",
+            "unit": "ratio", "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "long-context layer shape, n sweep", "B": B, "Hq": Hq,
+                       "Hkv": Hkv, "d": d, "window": w, "causal": True},
+            "sweep": rows}
     print(json.dumps(line), flush=True)
 
 

@@ -185,6 +185,35 @@ def test_window_covering_sequence_is_full_attention_on_gpu():
         assert (out - ref).abs().max().item() <= 1e-5
 
 
+@pytest.mark.parametrize("path", ["swa", "sa"])
+def test_full_causal_attention_comparator(path):
+    """The full-attention comparator: a window covering the sequence (w = n) on the same kernels.
+    At n = 4096 a workgroup's band spans 128 key chunks, i.e. two sigma segments, so this also
+    covers the segment reload path.  Sampled rows (first, last, random, a tile boundary) against
+    the oracle, bf16 bar."""
+    B, n, Hq, Hkv, d = 1, 4096, 8, 2, 128
+    w = n
+    host, dev = _data(31, B, n, Hq, Hkv, d, "bf16")
+    sig_dev, sig = _sigma(32, n)
+    q, k, v, _ = dev
+    if path == "swa":
+        out = ssw.swa_forward(q, k, v, w, True)
+    else:
+        out = ssw.sa_forward(q, k, v, sig_dev, w, True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(33)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 33, n - 2, n - 1],
+                                     rng.choice(n, size=40, replace=False)]))
+    qh, kh, vh, _ = host
+    if path == "swa":
+        ref = oracle.swa_rows(qh, kh, vh, w, True, rows)
+    else:
+        ref = oracle.sa_rows(qh, kh, vh, sig, w, True, rows)
+    got = out[:, rows]
+    err = _maxerr(got, ref, "bf16")
+    _say(f"full causal attention n={n} {path}: max err {err:.3e}")
+
+
 def test_timed_gated_call_matches_untimed():
     B, n, Hq, Hkv, d, w = 1, 700, 8, 2, 128, 64
     _, dev = _data(21, B, n, Hq, Hkv, d, "bf16")
