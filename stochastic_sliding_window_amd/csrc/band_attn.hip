@@ -61,6 +61,9 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 #ifndef SSW_WPE
 #define SSW_WPE 2  // waves per SIMD the register allocation is sized for
 #endif
+#ifndef SSW_STEP2
+#define SSW_STEP2 1  // bf16: two 32-key chunks per loop step
+#endif
 #ifndef SSW_PIPELINE
 #define SSW_PIPELINE 1  // scores of chunk c + 1 computed alongside the softmax of chunk c
 #endif
@@ -357,6 +360,9 @@ void band_attn_kernel(Params prm) {
   // 2j + 1 take the two halves of the stage STAGE + 1 + j.  Instruction i brings the rows of the
   // wave's columns i * (1024 / RB) ..., lane l granule l % kGran of column i * (1024 / RB) +
   // l / kGran; granules are XOR-swizzled by column so the epilogue's reads spread over banks.
+  // bf16 with a 4-slot ring: two chunks per loop step; the prologue then fetches one step
+  constexpr bool kStep2 = SSW_STEP2 && SSW_PIPELINE && kBf16 && Lay::kNS == 4;
+  constexpr int kPro = kStep2 ? 2 : Lay::kPF;
   // (needs kWaves / 2 ring stages besides the last chunk's)
   constexpr bool kPrefetchPartial =
       EPI == kEpiAddPartial && kBf16 && Lay::kNS - 1 >= (kWaves + 1) / 2;
@@ -403,7 +409,7 @@ void band_attn_kernel(Params prm) {
   __syncthreads();
   if constexpr (PERM) patch_sigma_tail(kbeg, min(nchunks, kSegChunks));
   // the first chunks of the first segment go in flight before Q is loaded, so the two overlap
-  static_for<Lay::kPF>([&](auto pf) {
+  static_for<kPro>([&](auto pf) {
     if (pf() < min(nchunks, kSegChunks)) dma_chunk(kbeg + pf() * kChunk, pf, kbeg);
   });
 
@@ -753,6 +759,127 @@ void band_attn_kernel(Params prm) {
     return sn;
   };
 
+
+  // bf16, two chunks per step: chunks ca and ca + 1 in ring slots STA and STA + 1 (hb: the second
+  // chunk exists).  Scores of both chunks (two independent MFMA chains), both masks, one column
+  // max and one lazy-reference check for the 64 keys, then P*V for both.  Per chunk the arithmetic
+  // is that of compute_s and softmax_pv.
+  auto mask16 = [&](int c, bool interior, int seg_key0, const f32x16& s, float* sm) {
+    const int kc0 = kbeg + c * kChunk;
+    int sk[16];
+    if constexpr (SIGMASK) {
+      const int* sp = sig_lds + (kc0 - seg_key0);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const u32x4 a = *(const u32x4*)(sp + 16 * half + 8 * h32);
+        const u32x4 bq = *(const u32x4*)(sp + 16 * half + 8 * h32 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sk[8 * half + e] = (int)a[e];
+          sk[8 * half + 4 + e] = (int)bq[e];
+        }
+      }
+    }
+    if (interior) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        bool ok = true;
+        if constexpr (SIGMASK) ok = sk[r] <= myorig;
+        sm[r] = ok ? s[r] : -INFINITY;
+      }
+    } else {
+      const int a = max(max(myslot - L, 0) - kc0, 0);
+      const int z = min(min(myslot + R, n - 1) - kc0, 31);
+      const uint32_t upto = z < 0 ? 0u : (0xFFFFFFFFu >> (31 - z));
+      const uint32_t from = a > 31 ? 0u : (0xFFFFFFFFu << a);
+      const uint32_t bm = (upto & from) >> (8 * h32);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        bool ok = (bm >> (16 * (r >> 3) + (r & 7))) & 1u;
+        if constexpr (SIGMASK) ok = ok & (sk[r] <= myorig);
+        sm[r] = ok ? s[r] : -INFINITY;
+      }
+    }
+  };
+  auto step2 = [&](int ca, auto sta_c, bool hb, bool int_a, bool int_b, int seg_key0) {
+    constexpr int STA = decltype(sta_c)::value;
+    if constexpr (kBf16) {
+      const char* Ka = smem + STA * Lay::kStageBytes;
+      const char* Kb = smem + (STA + 1) * Lay::kStageBytes;
+      f32x16 s_a = zero16(), s_b = zero16();
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Ka + k_off[kb]));
+        s_a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s_a, 0, 0, 0);
+      }
+      if (hb) {
+#pragma unroll
+        for (int kb = 0; kb < D / 16; ++kb) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kb + k_off[kb]));
+          s_b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s_b, 0, 0, 0);
+        }
+      }
+      float sm[32];
+      mask16(ca, int_a, seg_key0, s_a, sm);
+      if (hb) {
+        mask16(ca + 1, int_b, seg_key0, s_b, sm + 16);
+      } else {
+#pragma unroll
+        for (int r = 16; r < 32; ++r) sm[r] = -INFINITY;
+      }
+      float mraw = sm[0];
+#pragma unroll
+      for (int r = 1; r < 32; ++r) mraw = fmaxf(mraw, sm[r]);
+      mraw = pair_max(mraw);
+      const float mx = mraw * prm.scale_log2;
+      const bool need = mx > m_ref + kLazy;
+      // O is still exactly zero while the reference is -inf (every earlier key was masked), so
+      // the first raise of the reference needs no rescale
+      const bool rescale = need && m_ref != -INFINITY;
+      const float m_new = need ? mx : m_ref;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+      m_ref = m_new;
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int r = 0; r < 32; ++r)
+        pb[r >> 3][r & 7] =
+            (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sm[r], prm.scale_log2, -m_use));
+      if (__ballot(rescale)) {
+#pragma unroll
+        for (int t = 0; t < kOT; ++t) o[t] *= alpha;
+      }
+      // The row sum is taken over the bf16-rounded weights that enter the P*V product.
+      float psum = 0.f;
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[t][e], pb[t][e + 1]}, one2, psum, false);
+      l_run = l_run * alpha + psum;
+      auto pv = [&](const char* Kst, const bf16x8* pbc) {
+        const SSW_LDS char* vbase = (const SSW_LDS char*)Kst;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int db = 0; db < kOT; ++db) {
+            const SSW_LDS char* vp = vbase + v_off[db] + 16 * t * Lay::kRowBytes;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)vp);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (SSW_LDS s16x4*)(vp + 4 * Lay::kRowBytes));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+            const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pbc[t], o[db], 0, 0, 0);
+          }
+        }
+      };
+      pv(Ka, pb);
+      if (hb) pv(Kb, pb + 2);
+    }
+  };
+
   // ---- main loop over segments of at most kSegChunks chunks (one segment in practice)
   for (int sg = 0; sg < nseg; ++sg) {
     const int c0 = sg * kSegChunks;
@@ -768,11 +895,48 @@ void band_attn_kernel(Params prm) {
         __syncthreads();
         patch_sigma_tail(seg_key0, segc);
       }
-      static_for<Lay::kPF>([&](auto pf) {
+      static_for<kPro>([&](auto pf) {
         if (pf() < segc) dma_chunk(seg_key0 + pf() * kChunk, pf, seg_key0);
       });
     }
 
+#if SSW_STEP2 && SSW_PIPELINE
+    if constexpr (kStep2) {
+      // Steps of two chunks: step i uses ring slots 2i % 4 and 2i % 4 + 1; after its barrier
+      // (step i - 1 consumed) the next step's two chunks are fetched into step i - 1's slots.
+      auto active = [&](int c) { return wave_on && c >= c_first && c <= c_last; };
+      const int nsteps = (segc + 1) / 2;
+      for (int st0 = 0; st0 < nsteps; st0 += 2) {
+        static_for<2>([&](auto par) {
+          const int st = st0 + par();
+          if (st < nsteps) {
+            constexpr int kSlot = 2 * par();
+            constexpr int kFetchSlot = 2 * (1 - par());
+            const int ca = 2 * st;
+            const bool hb = ca + 1 < segc;
+            const bool fetch_a = ca + 2 < segc;
+            const bool fetch_b = ca + 3 < segc;
+            DmaRows ra, rb;
+            if (fetch_a) ra = dma_prep(seg_key0 + (ca + 2) * kChunk, seg_key0);
+            if (fetch_b) rb = dma_prep(seg_key0 + (ca + 3) * kChunk, seg_key0);
+            wait_vmcnt<0>();  // this step's chunks (the only loads in flight)
+            __syncthreads();  // and every wave's; the previous step's slots are free
+            if (fetch_a)
+              dma_issue(seg_key0 + (ca + 2) * kChunk, std::integral_constant<int, kFetchSlot>{}, ra);
+            if (fetch_b)
+              dma_issue(seg_key0 + (ca + 3) * kChunk,
+                        std::integral_constant<int, kFetchSlot + 1>{}, rb);
+            if constexpr (kPrefetchPartial)
+              if (sg == nseg - 1 && st == nsteps - 1 && wave_on)
+                dma_partial(hb ? kSlot + 1 : kSlot, out_off);
+            if (active(c0 + ca) || (hb && active(c0 + ca + 1)))
+              step2(c0 + ca, std::integral_constant<int, kSlot>{}, hb, is_interior(c0 + ca),
+                    hb && is_interior(c0 + ca + 1), seg_key0);
+          }
+        });
+      }
+    } else {
+#endif
 #if SSW_PIPELINE
     // Software pipeline: while chunk cs is consumed (softmax + P*V from its V), the scores of
     // chunk cs + 1 are already computed from its K, so each wave has independent MFMA work to
@@ -833,6 +997,9 @@ void band_attn_kernel(Params prm) {
         }
       });
     }
+#if SSW_STEP2 && SSW_PIPELINE
+    }
+#endif
   }
 #else
     // Chunk cs is consumed in iteration cs (scores, softmax, P*V) while chunks cs + 1 .. cs + kPF
