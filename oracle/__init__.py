@@ -13,6 +13,8 @@ definitions on the pages:
   fixed, published one that both sides implement independently).
 * attention.py   -- neighbour sets, SA / SWA / gated forward, and a second, permuted-space
   formulation of SA used to cross-check the first.
+* backward.py    -- the gradients of those forwards (chain rule through the definition, one
+  query row at a time), the rows' log-sum-exp, and sampled-row forms for large n.
 
 Sources (the pages):
   [SA-ja] "技術的概要：確率的アテンション" (gist.science/ja/paper/2604.00754) -- Stochastic
@@ -39,6 +41,14 @@ from .attention import (
     gated_forward,
     sa_forward_permuted_dense,
 )
+from .backward import (
+    attention_lse_rows,
+    attention_backward,
+    gated_backward,
+    attention_backward_query_rows,
+    attention_backward_key_rows,
+    attending_queries,
+)
 
 __all__ = [
     "splitmix64_stream",
@@ -53,4 +63,10 @@ __all__ = [
     "swa_forward",
     "gated_forward",
     "sa_forward_permuted_dense",
+    "attention_lse_rows",
+    "attention_backward",
+    "gated_backward",
+    "attention_backward_query_rows",
+    "attention_backward_key_rows",
+    "attending_queries",
 ]
