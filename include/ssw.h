@@ -1,6 +1,7 @@
 /*
  * ssw.h -- C ABI of libssw.so: Stochastic Attention (SA), sliding-window attention (SWA) and the
- * gated SA+SWA forward on AMD Instinct MI355X (gfx950).
+ * gated SA+SWA layer on AMD Instinct MI355X (gfx950): forward, and forward + backward for
+ * training.
  *
  * The operation (from the pages):
  *   [SA-ja] "技術的概要：確率的アテンション" (gist.science/ja/paper/2604.00754), 手法 › 中核メカニズム:
@@ -107,6 +108,79 @@ int ssw_gated_sa_swa_forward_timed(const void* q, const void* k, const void* v,
                                    const float* gates, void* out, int B, int n, int Hq, int Hkv,
                                    int d, int dtype, void* stream, void* ev_swa_start,
                                    void* ev_swa_end, void* ev_sa_start, void* ev_sa_end);
+
+/* ---- Training: forward with the rows' log-sum-exp, backward, gated forward and backward ----
+ *
+ * The pages pretrain a model from scratch with the gated layer ([SA-ja] 主要な貢献 item 3 and
+ * 結果, 事前学習), so the layer has a backward pass.  It is the exact gradient of the forward
+ * above (chain rule through its definition; no page prescribes more).  With A the attention
+ * output of a row (SA or SWA), y = g (.) A its gated form (g = 1 when no gate is given),
+ * P the row's softmax weights, s = 1/sqrt(d) and dy = dL/dy:
+ *   dV_j += P_j g dy,   dS_j = P_j (<g dy, V_j> - <g dy, A>),
+ *   dQ = s sum_j dS_j K_j,   dK_j += s dS_j Q,   dg = <dy, A>.
+ * The training calls take bf16 tensors only (SSW_EDTYPE otherwise); accumulation is fp32 and
+ * every bf16 result is rounded to nearest even at its store. */
+
+/* SA forward without a gate that also stores, for every row, lse = log sum_j exp(s <Q, K_j>)
+ * over the row's neighbours (natural log; the backward rebuilds P from it).
+ *   out       device [B, n, Hq, d]: A (no gate), fully overwritten.
+ *   lse       device float32 [B, n, Hq], indexed by original token; fully overwritten.
+ * Other arguments as in ssw_sa_forward (fp32 and bf16 both allowed here). */
+int ssw_sa_forward_lse(const void* q, const void* k, const void* v, const int32_t* sigma,
+                       int window, int causal, void* out, float* lse,
+                       int B, int n, int Hq, int Hkv, int d, int dtype, void* stream);
+
+/* The same for SWA (sigma must be NULL). */
+int ssw_swa_forward_lse(const void* q, const void* k, const void* v, const int32_t* sigma,
+                        int window, int causal, void* out, float* lse,
+                        int B, int n, int Hq, int Hkv, int d, int dtype, void* stream);
+
+/* SA backward of y = gate (.) A, A = SA(q, k, v; sigma, w, causal).
+ *   q, k, v, sigma, window, causal   as given to the forward.
+ *   gate      device float32 [B, n, Hq] or NULL (gate 1).
+ *   out, lse  A and lse as stored by ssw_sa_forward_lse.
+ *   dout      device [B, n, Hq, d]: dL/dy.
+ *   dq        device [B, n, Hq, d];  dk, dv  device [B, n, Hkv, d].  Written whole, or, when
+ *             accumulate = 1, the gradients are added to what they hold (each element read,
+ *             added in fp32, rounded once).
+ *   dgate     device float32 [B, n, Hq] or NULL: dL/dgate = <dy, A> per row (overwritten).
+ *   delta     device float32 [B, n, Hq]: scratch the call overwrites (g <dy, A> per row).
+ *   accumulate  0 or 1.
+ * Two kernels run back to back on `stream` (dQ, which also writes delta and dgate, then dK/dV).
+ * dq, dk, dv, dgate and delta must not overlap each other or the inputs.  bf16 only. */
+int ssw_sa_backward(const void* q, const void* k, const void* v, const int32_t* sigma,
+                    int window, int causal, const float* gate, const void* out, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, float* dgate, float* delta,
+                    int accumulate, int B, int n, int Hq, int Hkv, int d, int dtype, void* stream);
+
+/* The same for SWA (sigma must be NULL; out and lse from ssw_swa_forward_lse). */
+int ssw_swa_backward(const void* q, const void* k, const void* v, const int32_t* sigma,
+                     int window, int causal, const float* gate, const void* out,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     float* dgate, float* delta, int accumulate, int B, int n, int Hq, int Hkv,
+                     int d, int dtype, void* stream);
+
+/* Training forward of the gated layer: y_swa, lse_swa = SWA with lse; y_sa, lse_sa = SA with
+ * lse; then out = g_sa (.) y_sa + g_swa (.) y_swa from the stored bf16 values (one rounding).
+ * Three kernels on `stream`.  y_sa, y_swa device [B, n, Hq, d]; lse_sa, lse_swa device float32
+ * [B, n, Hq]; all overwritten.  Keep y_sa, lse_sa, y_swa, lse_swa for the backward.  bf16 only;
+ * other arguments as in ssw_gated_sa_swa_forward. */
+int ssw_gated_sa_swa_forward_train(const void* q, const void* k, const void* v,
+                                   const int32_t* sigma, int window, int causal,
+                                   const float* gates, void* out, void* y_sa, float* lse_sa,
+                                   void* y_swa, float* lse_swa, int B, int n, int Hq, int Hkv,
+                                   int d, int dtype, void* stream);
+
+/* Backward of the gated layer: dq, dk, dv (overwritten) = the SA path's gradients with gate g_sa
+ * plus the SWA path's with gate g_swa; dgates device float32 [2, B, n, Hq] or NULL receives
+ * (<dy, y_sa>, <dy, y_swa>).  delta is scratch as in ssw_sa_backward.  Four kernels on
+ * `stream`; the SWA path adds to the SA path's bf16 results, so dq, dk, dv are rounded twice. */
+int ssw_gated_sa_swa_backward(const void* q, const void* k, const void* v, const int32_t* sigma,
+                              int window, int causal, const float* gates, const void* y_sa,
+                              const float* lse_sa, const void* y_swa, const float* lse_swa,
+                              const void* dout, void* dq, void* dk, void* dv, float* dgates,
+                              float* delta, int B, int n, int Hq, int Hkv, int d, int dtype,
+                              void* stream);
 
 /* Host helpers (HOST pointers, no GPU needed). */
 

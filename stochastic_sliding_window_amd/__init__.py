@@ -1,4 +1,4 @@
-"""Stochastic Attention (SA), SWA and gated SA+SWA forward for AMD MI355X (gfx950).
+"""Stochastic Attention (SA), SWA and gated SA+SWA for AMD MI355X (gfx950): forward and backward.
 
 Thin ctypes binding over the C ABI of ``libssw.so`` (declared in ``include/ssw.h``).  Every
 function here only marshals arguments -- tensor checks, device pointers, the current HIP stream
@@ -12,6 +12,15 @@ The functions keep the C names without the ``ssw_`` prefix:
     gated_sa_swa_forward(q, k, v, sigma, window, causal, gates, out=None, events=None)
     make_permutation(seed, n) / inverse_permutation(sigma) / check_permutation(sigma)
     neighbor_mask(sigma, n, window, causal)
+
+Training (bf16):
+
+    sa_forward_lse(q, k, v, sigma, window, causal, out=None, lse=None) -> (out, lse)
+    swa_forward_lse(q, k, v, window, causal, out=None, lse=None) -> (out, lse)
+    sa_backward(q, k, v, sigma, window, causal, out, lse, dout, gate=None, ...) -> (dq, dk, dv, dgate)
+    swa_backward(q, k, v, window, causal, out, lse, dout, gate=None, ...) -> (dq, dk, dv, dgate)
+    gated_sa_swa_forward_train(q, k, v, sigma, window, causal, gates) -> (out, saved)
+    gated_sa_swa_backward(q, k, v, sigma, window, causal, gates, saved, dout) -> (dq, dk, dv, dgates)
 
 There is no fallback: if ``libssw.so`` has not been built, importing this package raises.
 """
@@ -33,7 +42,8 @@ import torch  # noqa: F401  (import order matters, see above)
 __all__ = [
     "SSWError", "LIB_PATH", "sa_forward", "swa_forward", "gated_sa_swa_forward",
     "make_permutation", "inverse_permutation", "check_permutation", "neighbor_mask",
-    "last_error", "F32", "BF16",
+    "last_error", "F32", "BF16", "sa_forward_lse", "swa_forward_lse", "sa_backward",
+    "swa_backward", "gated_sa_swa_forward_train", "gated_sa_swa_backward",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +82,24 @@ def _load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.ssw_gated_sa_swa_forward_timed.argtypes = fwd + [vp, vp, vp, vp]
     lib.ssw_gated_sa_swa_forward_timed.restype = ctypes.c_int
+    fwd_lse = [vp, vp, vp, i32p, i32, i32, vp, f32p, i32, i32, i32, i32, i32, i32, vp]
+    for name in ("ssw_sa_forward_lse", "ssw_swa_forward_lse"):
+        fn = getattr(lib, name)
+        fn.argtypes = fwd_lse
+        fn.restype = ctypes.c_int
+    bwd = [vp, vp, vp, i32p, i32, i32, f32p, vp, f32p, vp, vp, vp, vp, f32p, f32p, i32,
+           i32, i32, i32, i32, i32, i32, vp]
+    for name in ("ssw_sa_backward", "ssw_swa_backward"):
+        fn = getattr(lib, name)
+        fn.argtypes = bwd
+        fn.restype = ctypes.c_int
+    lib.ssw_gated_sa_swa_forward_train.argtypes = [vp, vp, vp, i32p, i32, i32, f32p, vp, vp, f32p,
+                                                   vp, f32p, i32, i32, i32, i32, i32, i32, vp]
+    lib.ssw_gated_sa_swa_forward_train.restype = ctypes.c_int
+    lib.ssw_gated_sa_swa_backward.argtypes = [vp, vp, vp, i32p, i32, i32, f32p, vp, f32p, vp, f32p,
+                                              vp, vp, vp, vp, f32p, f32p, i32, i32, i32, i32, i32,
+                                              i32, vp]
+    lib.ssw_gated_sa_swa_backward.restype = ctypes.c_int
     lib.ssw_make_permutation.argtypes = [ctypes.c_uint64, i32, i32p, i32p]
     lib.ssw_make_permutation.restype = ctypes.c_int
     lib.ssw_inverse_permutation.argtypes = [i32p, i32, i32p]
@@ -266,3 +294,156 @@ def neighbor_mask(sigma, n: int, window: int, causal: bool, device=None):
                                   _dev_ptr(bits), ctypes.c_void_p(
                                       torch.cuda.current_stream(bits.device).cuda_stream)))
     return bits
+
+
+# ------------------------------------------------------------------------------------------
+# training: forward with log-sum-exp, backward
+# ------------------------------------------------------------------------------------------
+
+def _prep_rows(t, shape, dtype, device, name):
+    """A given output/scratch tensor must be contiguous, on q's device, of the given shape/dtype."""
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype or \
+            not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous {dtype} {tuple(shape)} tensor on q's device")
+    return t
+
+
+def _prep_like(t, ref, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.shape != ref.shape or t.dtype != ref.dtype or \
+            not t.is_contiguous() or t.device != ref.device:
+        raise ValueError(f"{name} must be a contiguous tensor shaped and typed like {tuple(ref.shape)}")
+    return t
+
+
+def _forward_lse(fn, q, k, v, sigma, window, causal, out, lse):
+    torch = _torch()
+    out = _prep(q, k, v, out)
+    B, n, Hq, d = q.shape
+    lse = _prep_rows(lse, (B, n, Hq), torch.float32, q.device, "lse")
+    _check(fn(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sigma), int(window),
+              int(bool(causal)), _dev_ptr(out), _dev_ptr(lse), B, n, Hq, k.shape[2], d,
+              _dtype_code(q), _stream_handle(q)))
+    return out, lse
+
+
+def sa_forward_lse(q, k, v, sigma, window: int, causal: bool, out=None, lse=None):
+    """SA forward without gate that also returns each row's log-sum-exp (ssw_sa_forward_lse)."""
+    sigma = _prep_sigma(sigma, q.shape[1], q.device)
+    return _forward_lse(_lib.ssw_sa_forward_lse, q, k, v, sigma, window, causal, out, lse)
+
+
+def swa_forward_lse(q, k, v, window: int, causal: bool, out=None, lse=None):
+    """SWA forward that also returns each row's log-sum-exp (ssw_swa_forward_lse)."""
+    return _forward_lse(_lib.ssw_swa_forward_lse, q, k, v, None, window, causal, out, lse)
+
+
+def _backward(fn, q, k, v, sigma, window, causal, out, lse, dout, gate, dq, dk, dv, dgate,
+              delta, accumulate, want_dgate):
+    torch = _torch()
+    _prep(q, k, v, None if out is None else out)
+    B, n, Hq, d = q.shape
+    out = _prep_like(out, q, "out")
+    dout = _prep_like(dout, q, "dout")
+    lse = _prep_rows(lse, (B, n, Hq), torch.float32, q.device, "lse") if lse is not None else None
+    if lse is None:
+        raise ValueError("lse is required")
+    gate = _prep_gate(gate, (B, n, Hq), q.device)
+    if accumulate and (dq is None or dk is None or dv is None):
+        raise ValueError("accumulate needs dq, dk and dv to add to")
+    dq = _prep_like(dq, q, "dq") if dq is not None else torch.empty_like(q)
+    dk = _prep_like(dk, k, "dk") if dk is not None else torch.empty_like(k)
+    dv = _prep_like(dv, v, "dv") if dv is not None else torch.empty_like(v)
+    if dgate is None and want_dgate:
+        dgate = torch.empty((B, n, Hq), dtype=torch.float32, device=q.device)
+    elif dgate is not None:
+        dgate = _prep_rows(dgate, (B, n, Hq), torch.float32, q.device, "dgate")
+    delta = _prep_rows(delta, (B, n, Hq), torch.float32, q.device, "delta")
+    _check(fn(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sigma), int(window),
+              int(bool(causal)), _dev_ptr(gate), _dev_ptr(out), _dev_ptr(lse), _dev_ptr(dout),
+              _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv), _dev_ptr(dgate), _dev_ptr(delta),
+              int(bool(accumulate)), B, n, Hq, k.shape[2], d, _dtype_code(q), _stream_handle(q)))
+    return dq, dk, dv, dgate
+
+
+def sa_backward(q, k, v, sigma, window: int, causal: bool, out, lse, dout, gate=None, dq=None,
+                dk=None, dv=None, dgate=None, delta=None, accumulate=False, want_dgate=True):
+    """Gradients of y = gate * SA(q, k, v) given dout = dL/dy (ssw_sa_backward).
+
+    out and lse come from sa_forward_lse.  Returns (dq, dk, dv, dgate); with accumulate=True the
+    gradients are added to the given dq, dk, dv.
+    """
+    sigma = _prep_sigma(sigma, q.shape[1], q.device)
+    return _backward(_lib.ssw_sa_backward, q, k, v, sigma, window, causal, out, lse, dout, gate,
+                     dq, dk, dv, dgate, delta, accumulate, want_dgate)
+
+
+def swa_backward(q, k, v, window: int, causal: bool, out, lse, dout, gate=None, dq=None, dk=None,
+                 dv=None, dgate=None, delta=None, accumulate=False, want_dgate=True):
+    """Gradients of y = gate * SWA(q, k, v) given dout (ssw_swa_backward)."""
+    return _backward(_lib.ssw_swa_backward, q, k, v, None, window, causal, out, lse, dout, gate,
+                     dq, dk, dv, dgate, delta, accumulate, want_dgate)
+
+
+def gated_sa_swa_forward_train(q, k, v, sigma, window: int, causal: bool, gates, out=None,
+                               saved=None):
+    """Training forward of the gated layer (ssw_gated_sa_swa_forward_train).
+
+    Returns (out, saved) with saved = (y_sa, lse_sa, y_swa, lse_swa) for the backward.
+    """
+    torch = _torch()
+    out = _prep(q, k, v, out)
+    B, n, Hq, d = q.shape
+    sigma = _prep_sigma(sigma, n, q.device)
+    if gates is None:
+        raise ValueError("gates are required")
+    gates = _prep_gate(gates, (2, B, n, Hq), q.device)
+    if saved is None:
+        saved = (torch.empty_like(q), torch.empty((B, n, Hq), dtype=torch.float32, device=q.device),
+                 torch.empty_like(q), torch.empty((B, n, Hq), dtype=torch.float32, device=q.device))
+    y_sa, lse_sa, y_swa, lse_swa = saved
+    y_sa, y_swa = _prep_like(y_sa, q, "y_sa"), _prep_like(y_swa, q, "y_swa")
+    lse_sa = _prep_rows(lse_sa, (B, n, Hq), torch.float32, q.device, "lse_sa")
+    lse_swa = _prep_rows(lse_swa, (B, n, Hq), torch.float32, q.device, "lse_swa")
+    _check(_lib.ssw_gated_sa_swa_forward_train(
+        _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sigma), int(window), int(bool(causal)),
+        _dev_ptr(gates), _dev_ptr(out), _dev_ptr(y_sa), _dev_ptr(lse_sa), _dev_ptr(y_swa),
+        _dev_ptr(lse_swa), B, n, Hq, k.shape[2], d, _dtype_code(q), _stream_handle(q)))
+    return out, (y_sa, lse_sa, y_swa, lse_swa)
+
+
+def gated_sa_swa_backward(q, k, v, sigma, window: int, causal: bool, gates, saved, dout, dq=None,
+                          dk=None, dv=None, dgates=None, delta=None, want_dgates=True):
+    """Gradients of the gated layer (ssw_gated_sa_swa_backward); saved from the training forward.
+
+    Returns (dq, dk, dv, dgates) with dgates [2, B, n, Hq] (or None if want_dgates is False).
+    """
+    torch = _torch()
+    _prep(q, k, v, None)
+    B, n, Hq, d = q.shape
+    sigma = _prep_sigma(sigma, n, q.device)
+    gates = _prep_gate(gates, (2, B, n, Hq), q.device)
+    if gates is None:
+        raise ValueError("gates are required")
+    y_sa, lse_sa, y_swa, lse_swa = saved
+    y_sa, y_swa = _prep_like(y_sa, q, "y_sa"), _prep_like(y_swa, q, "y_swa")
+    lse_sa = _prep_rows(lse_sa, (B, n, Hq), torch.float32, q.device, "lse_sa")
+    lse_swa = _prep_rows(lse_swa, (B, n, Hq), torch.float32, q.device, "lse_swa")
+    dout = _prep_like(dout, q, "dout")
+    dq = _prep_like(dq, q, "dq") if dq is not None else torch.empty_like(q)
+    dk = _prep_like(dk, k, "dk") if dk is not None else torch.empty_like(k)
+    dv = _prep_like(dv, v, "dv") if dv is not None else torch.empty_like(v)
+    if dgates is None and want_dgates:
+        dgates = torch.empty((2, B, n, Hq), dtype=torch.float32, device=q.device)
+    elif dgates is not None:
+        dgates = _prep_rows(dgates, (2, B, n, Hq), torch.float32, q.device, "dgates")
+    delta = _prep_rows(delta, (B, n, Hq), torch.float32, q.device, "delta")
+    _check(_lib.ssw_gated_sa_swa_backward(
+        _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sigma), int(window), int(bool(causal)),
+        _dev_ptr(gates), _dev_ptr(y_sa), _dev_ptr(lse_sa), _dev_ptr(y_swa), _dev_ptr(lse_swa),
+        _dev_ptr(dout), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv), _dev_ptr(dgates),
+        _dev_ptr(delta), B, n, Hq, k.shape[2], d, _dtype_code(q), _stream_handle(q)))
+    return dq, dk, dv, dgates

@@ -26,7 +26,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["ssw_api.cpp", "band_attn.hip"]
+SOURCES = ["ssw_api.cpp", "band_attn.hip", "band_attn_bwd.hip"]
 
 
 def hipcc() -> str:

@@ -31,6 +31,8 @@ struct BandLaunch {
   bool causal;
   bool perm;
   int epilogue;          // Epilogue
+  // optional: the natural-log log-sum-exp of every row, fp32 [B, n, Hq] at original positions
+  float* lse = nullptr;
   // optional hipEvent_t pair attached to the kernel's dispatch: recorded when the kernel starts
   // and when it ends (no separate event packets around it)
   void* ev_start = nullptr;
@@ -38,6 +40,38 @@ struct BandLaunch {
 };
 
 hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream);
+
+// The backward of one band-attention layer y = gate * A (A = the attention output), bf16 only.
+// Two launches: the dQ kernel (which also stores Delta = gate * rowsum(dout * A) and, if dgate
+// is set, dgate = rowsum(dout * A)), then the dK/dV kernel that reads Delta.
+struct BandBwdLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;          // A, [B, n, Hq, d]
+  const void* dout;       // dL/dy, [B, n, Hq, d]
+  const float* lse;       // [B, n, Hq], natural log
+  const float* gate;      // [B, n, Hq] or nullptr (gate 1)
+  const int32_t* sigma;   // device int32[n] when perm
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dgate;           // [B, n, Hq] or nullptr
+  float* delta;           // [B, n, Hq] scratch, overwritten
+  int B, n, Hq, Hkv, d;
+  int window;             // already clamped to [1, n]
+  bool causal;
+  bool perm;
+  bool accumulate;        // add into dq, dk, dv instead of overwriting them
+  void* ev[4] = {nullptr, nullptr, nullptr, nullptr};  // optional dispatch events: dq start/stop,
+                                                       // dk/dv start/stop
+};
+
+hipError_t launch_band_attn_bwd(const BandBwdLaunch& a, hipStream_t stream);
+
+// out = g_sa * y_sa + g_swa * y_swa for bf16 rows of d elements; gates [2, rows] fp32.
+hipError_t launch_gate_combine(const void* y_sa, const void* y_swa, const float* gates,
+                               void* out, int64_t rows, int d, hipStream_t stream);
 
 // bits [n][ceil(n/32)] uint32, overwritten.  sigma may be nullptr (identity).
 hipError_t launch_neighbor_mask(const int32_t* sigma, int n, int window, bool causal,

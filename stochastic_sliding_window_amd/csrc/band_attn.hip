@@ -226,6 +226,7 @@ struct Params {
   const int32_t* sigma;
   const float* gate;
   char* out;
+  float* lse;        // natural-log log-sum-exp of each row [B, n, Hq], or nullptr
   int B, n, Hq, Hkv, G;
   int L, R;          // band: key slots [p - L, p + R]
   float scale_log2;  // log2(e) / sqrt(d)
@@ -1047,6 +1048,11 @@ void band_attn_kernel(Params prm) {
   // ---- epilogue: normalise, gate, scatter to original row sigma[p]
   const float l_tot = pair_sum(l_run);
   if (!colvalid) return;
+  // The row's log-sum-exp for a backward pass.  Every row holds its own token, so m_ref is finite
+  // and l_tot >= 1 here; l_tot sums exp2 of the scaled scores minus m_ref.
+  if (prm.lse && h32 == 0)
+    prm.lse[((int64_t)b * n + myorig) * prm.Hq + h] =
+        (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   const float f = __builtin_amdgcn_rcpf(l_tot) * gate_v;
   char* orow = prm.out + qrow_elems * (int64_t)sizeof(T);
   const char* prow = nullptr;  // this column's prefetched intermediate row (LDS)
@@ -1167,6 +1173,7 @@ hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream) {
   prm.sigma = a.sigma;
   prm.gate = a.gate;
   prm.out = (char*)a.out;
+  prm.lse = a.lse;
   prm.B = a.B;
   prm.n = a.n;
   prm.Hq = a.Hq;

@@ -1,0 +1,673 @@
+// Backward pass of band attention on gfx950 (SA, SWA and the gated layer), and the gate combine
+// of the training forward.  bf16 inputs and outputs, fp32 accumulation.
+//
+// What is computed.  The forward is [SA-ja] "技術的概要：確率的アテンション", 中核メカニズム steps
+// 1-3 with the causal rule of 理論的性質 ([HYB] ハイブリッドアーキテクチャの定義 for SWA): the query
+// at permuted slot p (original token sigma[p]) attends to the keys at slots q with
+// |p - q| <= w - 1, in causal mode only those with sigma[q] <= sigma[p].  A layer output is
+// y = g * A with g a gate value per (token, head) (1 when absent).  Its gradient, by the chain
+// rule through that definition, with P rebuilt from the forward's log-sum-exp:
+//   dP = (g dy) V^T,  Delta = rowsum(g dy * A),  dS = P * (dP - Delta),
+//   dQ = s dS K,  dK = s dS^T Q,  dV = P^T (g dy),  dg = rowsum(dy * A)   (s = 1/sqrt(d)).
+//
+// Mapping onto the chip: two kernels and no atomics, so every gradient row is written once.
+//   * bwd_dq_kernel is query-major with the forward's tiling: a workgroup owns 128 (slot, head)
+//     columns of one KV head, 32 per wave.  Its prologue loads the columns' Q and dy rows (MFMA
+//     B operands, kept in registers), forms Delta and dg from dy and A, and stores Delta for the
+//     second kernel.  Its loop streams the band's 32-key K/V chunks: S^T = K Q^T and
+//     dP^T = V (dy)^T share the row-read A operands, and dQ^T += K^T dS^T takes K^T from
+//     transposed LDS reads, with dS^T already in B-operand order.
+//   * bwd_dkdv_kernel is key-major: a wave owns 32 key slots of one KV head (their K and V rows
+//     are B operands in registers), the workgroup 128.  Its loop streams chunks of 32 query
+//     columns (Q and dy rows plus each column's log-sum-exp, Delta, gate, slot and original
+//     index): S = Q K^T and dP = dy V^T leave P and dS with one key per lane, which is the B
+//     operand of dV^T += (dy)^T (g P) and dK^T += Q^T dS.
+//   * Chunks are gathered through sigma into registers one chunk ahead and written to a
+//     two-stage LDS ring.  Rows sit in MFMA row order, XOR-swizzled by 16-byte granule, which
+//     serves the row reads of the score products and the transposed reads (ds_read_b64_tr_b16)
+//     of the gradient products alike.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+
+#include "band_attn.h"
+
+namespace ssw {
+namespace bwd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define SSW_LDS __attribute__((address_space(3)))
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kChunk = 32;     // keys (dq kernel) or query columns (dk/dv kernel) per chunk
+constexpr int kTile = 128;     // columns (dq kernel) or key slots (dk/dv kernel) per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Params {
+  const char* q;
+  const char* k;
+  const char* v;
+  const char* o;
+  const char* dout;
+  const float* lse;
+  const float* gate;
+  const int32_t* sigma;
+  char* dq;
+  char* dk;
+  char* dv;
+  float* dgate;
+  float* delta;
+  int B, n, Hq, Hkv, G;
+  int L, R;          // band: key slots [p - L, p + R] of query slot p
+  float scale_log2;  // log2(e) / sqrt(d)
+  float scale;       // 1 / sqrt(d)
+  int ntiles;        // tiles per (batch row, KV head)
+  int nblocks;       // ntiles * B * Hkv
+  int accumulate;
+};
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// lanes l and l ^ 32 hold the same column; v_permlane32_swap exchanges the halves (inline asm:
+// the builtin's two results were folded into one when both inputs were the same value)
+__device__ __forceinline__ float pair_sum(float x) {
+  float a = x, c = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(c));
+  return a + c;
+}
+
+// MFMA 32x32 row r of a chunk holds chunk entry rho(r), where rho swaps bits 2 and 3 of r: then
+// output register i of lane half h holds entry 16(i / 8) + 8h + i % 8, which is the k order of
+// the B operand of the next product.  rho is its own inverse.
+__device__ __forceinline__ int rho(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Consecutive workgroup ids go to the 8 XCDs in turn; renumber them so each XCD (own L2) gets a
+// contiguous run of tiles, whose K/V or Q/dy halos overlap.
+__device__ __forceinline__ int xcd_local_order(int i, int nblocks) {
+  const int per = nblocks / 8;
+  if (i < per * 8) return (i % 8) * per + i / 8;
+  return i;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+// Store four consecutive values of a gradient row (8 bytes), adding the stored ones if asked.
+__device__ __forceinline__ void store4(char* p, float y0, float y1, float y2, float y3, bool add) {
+  u32x2* dst = (u32x2*)p;
+  if (add) {
+    const u32x2 old = *dst;
+    y0 += bf_lo(old[0]);
+    y1 += bf_hi(old[0]);
+    y2 += bf_lo(old[1]);
+    y3 += bf_hi(old[1]);
+  }
+  *dst = u32x2{pack2(y0, y1), pack2(y2, y3)};
+}
+
+template <int D>
+struct Lay {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kGran = D / 8;                // 16-byte granules per row
+  static constexpr int kMat = kChunk * kRowBytes;    // one 32-row matrix of a stage
+  static constexpr int kPer = 2 * kChunk * kGran / kThreads;  // granules per thread per chunk
+  static constexpr int kKB = D / 16;                 // k steps of the score products
+  static constexpr int kDB = D / 32;                 // 32-row d blocks of a gradient accumulator
+  static_assert(kPer >= 1 && 2 * kChunk * kGran == kPer * kThreads, "chunk split");
+};
+
+// LDS offset of granule `gran` of MFMA row `row` within a stage matrix
+template <int D>
+__device__ __forceinline__ int gran_off(int row, int gran) {
+  return row * Lay<D>::kRowBytes + ((gran ^ (row & (Lay<D>::kGran - 1))) << 4);
+}
+
+// Per-lane LDS offsets of the transposed reads of a stage matrix.  The A operand of a gradient
+// product (32 d-rows x 16 chunk entries) for k block t comes from two ds_read_b64_tr_b16: lane j
+// of 16-lane group grp points at 4 d-values of chunk entry 16t + 8h + 4*hi + j/4 at
+// d = 32db + 16(grp % 2) + 4(j % 4); after the read, lane l holds row d = 32db + l % 32 for
+// entries 16t + 8h + [0, 8).  Entry e sits at row rho(e); adding 16t to e adds 16t to the row,
+// which leaves the swizzle unchanged, so t is a constant offset.
+template <int D>
+__device__ __forceinline__ int tr_off(int lane, int db, int hi) {
+  const int grp = lane >> 4;
+  const int j = lane & 15;
+  const int e = 8 * (lane >> 5) + 4 * hi + (j >> 2);
+  const int row = rho(e);
+  const int d = 32 * db + 16 * (grp & 1) + 4 * (j & 3);
+  return row * Lay<D>::kRowBytes + (((d >> 3) ^ (row & (Lay<D>::kGran - 1))) << 4) + ((d & 7) << 1);
+}
+
+__device__ __forceinline__ bf16x8 tr_read(const char* lo_p, const char* hi_p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)(const SSW_LDS char*)lo_p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)(const SSW_LDS char*)hi_p);
+  // whole-vector casts only (element-wise assembly of such operands was miscompiled)
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+  const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+}
+
+__device__ __forceinline__ bf16x8 ld_bf16x8(const char* p) {
+  return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
+}
+
+// ------------------------------------------------------------------------------------------------
+// dQ (and Delta, dg): query-major
+// ------------------------------------------------------------------------------------------------
+template <int D, bool PERM, bool SIGMASK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(Params prm) {
+  using LY = Lay<D>;
+  constexpr int kStage = 2 * LY::kMat + kChunk * 4;  // K, V, sigma of the chunk's keys
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h32 = lane >> 5;
+  const int r32 = lane & 31;
+  const int n = prm.n;
+  const int G = prm.G;
+  const int L = prm.L;
+  const int R = prm.R;
+  const int nG = n * G;
+
+  const int blk = xcd_local_order(blockIdx.x, prm.nblocks);
+  const int tile = blk % prm.ntiles;
+  const int bg = blk / prm.ntiles;
+  const int b = bg / prm.Hkv;
+  const int g = bg - b * prm.Hkv;
+
+  // ---- columns: column c is (slot c / G, query head g * G + c % G)
+  const int col0_wg = tile * kTile;
+  const int col0_w = col0_wg + wave * 32;
+  const int mycol = col0_w + r32;
+  const bool colvalid = mycol < nG;
+  const int mycol_c = colvalid ? mycol : nG - 1;
+  const int myslot = mycol_c / G;
+  const int h = g * G + (mycol_c - myslot * G);
+  const int myorig = PERM ? prm.sigma[myslot] : myslot;
+  const bool wave_on = col0_w < nG;
+  const int w_slo = min(col0_w, nG - 1) / G;
+  const int w_shi = min(col0_w + 31, nG - 1) / G;
+  const int S_lo = col0_wg / G;
+  const int S_hi = min(col0_wg + kTile - 1, nG - 1) / G;
+  const int kbeg = max(0, S_lo - L);
+  const int kend = min(n - 1, S_hi + R);
+  const int nchunks = (kend - kbeg) / kChunk + 1;
+  const int c_first = (max(0, w_slo - L) - kbeg) / kChunk;
+  const int c_last = (min(n - 1, w_shi + R) - kbeg) / kChunk;
+
+  // ---- prologue: Q and dy rows as B operands (k step kb holds d = 16kb + 8h32 + [0, 8)),
+  // Delta and dg from dy and A
+  const int64_t rowq = ((int64_t)b * n + myorig) * prm.Hq + h;
+  const char* qrow = prm.q + rowq * LY::kRowBytes;
+  const char* drow = prm.dout + rowq * LY::kRowBytes;
+  const char* arow = prm.o + rowq * LY::kRowBytes;
+  bf16x8 qf[LY::kKB], df[LY::kKB];
+  float dot = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < LY::kKB; ++kb) {
+    const int off = (16 * kb + 8 * h32) * 2;
+    qf[kb] = ld_bf16x8(qrow + off);
+    const u32x4 dw = *(const u32x4*)(drow + off);
+    const u32x4 aw = *(const u32x4*)(arow + off);
+    df[kb] = __builtin_bit_cast(bf16x8, dw);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dot = __builtin_fmaf(bf_lo(dw[e]), bf_lo(aw[e]), dot);
+      dot = __builtin_fmaf(bf_hi(dw[e]), bf_hi(aw[e]), dot);
+    }
+  }
+  dot = pair_sum(dot);
+  const float gate_v = prm.gate ? prm.gate[rowq] : 1.0f;
+  const float delta = gate_v * dot;
+  const float lse2 = prm.lse[rowq] * kLog2e;
+  if (colvalid && h32 == 0) {
+    prm.delta[rowq] = delta;
+    if (prm.dgate) prm.dgate[rowq] = dot;
+  }
+
+  // ---- chunk staging: this thread's granules of the chunk's K and V rows, one chunk ahead
+  u32x4 st_regs[LY::kPer];
+  int st_sig = 0;
+  auto load_chunk = [&](int c) {
+    const int kc0 = kbeg + c * kChunk;
+#pragma unroll
+    for (int i = 0; i < LY::kPer; ++i) {
+      const int gi = i * kThreads + tid;
+      const int mat = gi / (kChunk * LY::kGran);
+      const int rem = gi - mat * (kChunk * LY::kGran);
+      const int row = rem / LY::kGran;
+      const int gran = rem - row * LY::kGran;
+      const int key = kc0 + rho(row);
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (key < n) {
+        const int tok = PERM ? prm.sigma[key] : key;
+        const char* src = (mat ? prm.v : prm.k) +
+                          ((((int64_t)b * n + tok) * prm.Hkv + g) * D + gran * 8) * 2;
+        val = *(const u32x4*)src;
+      }
+      st_regs[i] = val;
+    }
+    if (tid < kChunk) {
+      const int key = kc0 + tid;
+      st_sig = key < n ? (PERM ? prm.sigma[key] : key) : INT_MAX;
+    }
+  };
+  auto store_chunk = [&](int st) {
+    char* base = smem + st * kStage;
+#pragma unroll
+    for (int i = 0; i < LY::kPer; ++i) {
+      const int gi = i * kThreads + tid;
+      const int mat = gi / (kChunk * LY::kGran);
+      const int rem = gi - mat * (kChunk * LY::kGran);
+      const int row = rem / LY::kGran;
+      const int gran = rem - row * LY::kGran;
+      *(u32x4*)(base + mat * LY::kMat + gran_off<D>(row, gran)) = st_regs[i];
+    }
+    if (tid < kChunk) ((int*)(base + 2 * LY::kMat))[tid] = st_sig;
+  };
+
+  int k_off[LY::kKB];
+#pragma unroll
+  for (int kb = 0; kb < LY::kKB; ++kb) k_off[kb] = gran_off<D>(r32, 2 * kb + h32);
+  int t_off[LY::kDB][2];
+#pragma unroll
+  for (int db = 0; db < LY::kDB; ++db) {
+    t_off[db][0] = tr_off<D>(lane, db, 0);
+    t_off[db][1] = tr_off<D>(lane, db, 1);
+  }
+
+  f32x16 acc[LY::kDB];
+#pragma unroll
+  for (int db = 0; db < LY::kDB; ++db) acc[db] = zero16();
+
+  load_chunk(0);
+  for (int c = 0; c < nchunks; ++c) {
+    const int st = c & 1;
+    // stage st was last read in iteration c - 2, before every wave passed barrier c - 1
+    store_chunk(st);
+    __syncthreads();
+    if (c + 1 < nchunks) load_chunk(c + 1);
+    if (!wave_on || c < c_first || c > c_last) continue;
+    const char* Kst = smem + st * kStage;
+    const char* Vst = Kst + LY::kMat;
+    const int* sg = (const int*)(Kst + 2 * LY::kMat);
+
+    // S^T[key][col] = <K, Q>, dP^T[key][col] = <V, dy>; output register i of lane half h32 holds
+    // key 16(i / 8) + 8h32 + i % 8 of the chunk
+    f32x16 s = zero16();
+    f32x16 dp = zero16();
+#pragma unroll
+    for (int kb = 0; kb < LY::kKB; ++kb) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Kst + k_off[kb]), qf[kb], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Vst + k_off[kb]), df[kb], dp, 0, 0, 0);
+    }
+    const int kc0 = kbeg + c * kChunk;
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = 16 * (r >> 3) + 8 * h32 + (r & 7);
+      const int key = kc0 + e;
+      bool ok = key >= myslot - L && key <= myslot + R && key < n;
+      if constexpr (SIGMASK) ok = ok && sg[e] <= myorig;
+      const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -lse2)) : 0.f;
+      dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gate_v, dp[r], -delta));
+    }
+    // dQ^T[d][col] += K^T[d][key] dS^T[key][col]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int db = 0; db < LY::kDB; ++db) {
+        const char* kt = Kst + 16 * t * LY::kRowBytes;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kt + t_off[db][0], kt + t_off[db][1]),
+                                                          dsb[t], acc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: dQ row of the column at its original token; register 4a + u of block db holds
+  // d = 32db + 8a + 4h32 + u
+  if (!colvalid) return;
+  char* dqrow = prm.dq + rowq * LY::kRowBytes;
+#pragma unroll
+  for (int db = 0; db < LY::kDB; ++db) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * db + 8 * a + 4 * h32;
+      store4(dqrow + 2 * d0, acc[db][4 * a] * prm.scale, acc[db][4 * a + 1] * prm.scale,
+             acc[db][4 * a + 2] * prm.scale, acc[db][4 * a + 3] * prm.scale, prm.accumulate != 0);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// dK, dV: key-major
+// ------------------------------------------------------------------------------------------------
+// At d = 128 the K/V operands and the two accumulators alone take 192 registers per lane, so
+// the kernel is sized for one wave per SIMD (up to 512 registers, no spills).
+template <int D>
+constexpr int kDkdvWaves = D >= 128 ? 1 : 2;
+
+template <int D, bool PERM, bool SIGMASK>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kDkdvWaves<D>, kDkdvWaves<D>)))
+void bwd_dkdv_kernel(Params prm) {
+  using LY = Lay<D>;
+  // per stage: Q rows, dy rows, then per column log2-domain lse, Delta, gate, slot, original index
+  constexpr int kMetaOff = 2 * LY::kMat;
+  constexpr int kStage = kMetaOff + 5 * kChunk * 4;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h32 = lane >> 5;
+  const int r32 = lane & 31;
+  const int n = prm.n;
+  const int G = prm.G;
+  const int L = prm.L;
+  const int R = prm.R;
+  const int nG = n * G;
+
+  const int blk = xcd_local_order(blockIdx.x, prm.nblocks);
+  const int tile = blk % prm.ntiles;
+  const int bg = blk / prm.ntiles;
+  const int b = bg / prm.Hkv;
+  const int g = bg - b * prm.Hkv;
+
+  // ---- key slots of this workgroup / wave / lane
+  const int K0 = tile * kTile;
+  const int kw0 = K0 + wave * 32;
+  const int myk = kw0 + r32;
+  const bool keyvalid = myk < n;
+  const int myk_c = keyvalid ? myk : n - 1;
+  const int ktok = PERM ? prm.sigma[myk_c] : myk_c;
+  const bool wave_on = kw0 < n;
+  // key q is in the band of the query slots [q - R, q + L]
+  const int khi_wg = min(K0 + kTile - 1, n - 1);
+  const int col_lo = max(0, K0 - R) * G;
+  const int col_hi = min(n - 1, khi_wg + L) * G + G - 1;
+  const int nchunks = (col_hi - col_lo) / kChunk + 1;
+  const int wk_lo = min(kw0, n - 1);
+  const int wk_hi = min(kw0 + 31, n - 1);
+  const int c_first = (max(0, wk_lo - R) * G - col_lo) / kChunk;
+  const int c_last = (min(n - 1, wk_hi + L) * G + G - 1 - col_lo) / kChunk;
+
+  // ---- K and V rows of the lane's key as B operands (k step kb holds d = 16kb + 8h32 + [0, 8))
+  const int64_t krow = ((int64_t)b * n + ktok) * prm.Hkv + g;
+  bf16x8 kf[LY::kKB], vf[LY::kKB];
+#pragma unroll
+  for (int kb = 0; kb < LY::kKB; ++kb) {
+    const int off = (16 * kb + 8 * h32) * 2;
+    kf[kb] = ld_bf16x8(prm.k + krow * LY::kRowBytes + off);
+    vf[kb] = ld_bf16x8(prm.v + krow * LY::kRowBytes + off);
+  }
+
+  // ---- chunk staging: Q and dy rows of 32 query columns plus their per-column values
+  u32x4 st_regs[LY::kPer];
+  float m_lse2 = 0.f, m_delta = 0.f, m_gate = 0.f;
+  int m_slot = 0, m_orig = 0;
+  auto load_chunk = [&](int c) {
+    const int c0 = col_lo + c * kChunk;
+#pragma unroll
+    for (int i = 0; i < LY::kPer; ++i) {
+      const int gi = i * kThreads + tid;
+      const int mat = gi / (kChunk * LY::kGran);
+      const int rem = gi - mat * (kChunk * LY::kGran);
+      const int row = rem / LY::kGran;
+      const int gran = rem - row * LY::kGran;
+      const int col = c0 + rho(row);
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (col < nG) {
+        const int slot = col / G;
+        const int tok = PERM ? prm.sigma[slot] : slot;
+        const char* src = (mat ? prm.dout : prm.q) +
+                          ((((int64_t)b * n + tok) * prm.Hq + g * G + (col - slot * G)) * D +
+                           gran * 8) * 2;
+        val = *(const u32x4*)src;
+      }
+      st_regs[i] = val;
+    }
+    if (tid < kChunk) {
+      const int col = c0 + tid;
+      if (col < nG) {
+        const int slot = col / G;
+        const int tok = PERM ? prm.sigma[slot] : slot;
+        const int64_t row = ((int64_t)b * n + tok) * prm.Hq + g * G + (col - slot * G);
+        m_lse2 = prm.lse[row] * kLog2e;
+        m_delta = prm.delta[row];
+        m_gate = prm.gate ? prm.gate[row] : 1.0f;
+        m_slot = slot;
+        m_orig = tok;
+      } else {
+        // no key passes the band test (q <= slot + R fails) or the causal test
+        m_lse2 = 0.f;
+        m_delta = 0.f;
+        m_gate = 0.f;
+        m_slot = INT_MIN / 4;
+        m_orig = -1;
+      }
+    }
+  };
+  auto store_chunk = [&](int st) {
+    char* base = smem + st * kStage;
+#pragma unroll
+    for (int i = 0; i < LY::kPer; ++i) {
+      const int gi = i * kThreads + tid;
+      const int mat = gi / (kChunk * LY::kGran);
+      const int rem = gi - mat * (kChunk * LY::kGran);
+      const int row = rem / LY::kGran;
+      const int gran = rem - row * LY::kGran;
+      *(u32x4*)(base + mat * LY::kMat + gran_off<D>(row, gran)) = st_regs[i];
+    }
+    if (tid < kChunk) {
+      float* mf = (float*)(base + kMetaOff);
+      int* mi = (int*)(base + kMetaOff);
+      mf[tid] = m_lse2;
+      mf[kChunk + tid] = m_delta;
+      mf[2 * kChunk + tid] = m_gate;
+      mi[3 * kChunk + tid] = m_slot;
+      mi[4 * kChunk + tid] = m_orig;
+    }
+  };
+
+  int a_off[LY::kKB];
+#pragma unroll
+  for (int kb = 0; kb < LY::kKB; ++kb) a_off[kb] = gran_off<D>(r32, 2 * kb + h32);
+  int t_off[LY::kDB][2];
+#pragma unroll
+  for (int db = 0; db < LY::kDB; ++db) {
+    t_off[db][0] = tr_off<D>(lane, db, 0);
+    t_off[db][1] = tr_off<D>(lane, db, 1);
+  }
+
+  f32x16 dk[LY::kDB], dv[LY::kDB];
+#pragma unroll
+  for (int db = 0; db < LY::kDB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+
+  load_chunk(0);
+  for (int c = 0; c < nchunks; ++c) {
+    const int st = c & 1;
+    store_chunk(st);
+    __syncthreads();
+    if (c + 1 < nchunks) load_chunk(c + 1);
+    if (!wave_on || c < c_first || c > c_last) continue;
+    const char* Qst = smem + st * kStage;
+    const char* Dst = Qst + LY::kMat;
+    const float* mf = (const float*)(Qst + kMetaOff);
+    const int* mi = (const int*)(Qst + kMetaOff);
+
+    // S[col][key] = <Q, K>, dP[col][key] = <dy, V>; output register i of lane half h32 holds
+    // column 16(i / 8) + 8h32 + i % 8 of the chunk, for the lane's key
+    f32x16 s = zero16();
+    f32x16 dp = zero16();
+#pragma unroll
+    for (int kb = 0; kb < LY::kKB; ++kb) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Qst + a_off[kb]), kf[kb], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Dst + a_off[kb]), vf[kb], dp, 0, 0, 0);
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = 16 * (r >> 3) + 8 * h32 + (r & 7);
+      const int slot = mi[3 * kChunk + e];
+      bool ok = myk >= slot - L && myk <= slot + R;
+      if constexpr (SIGMASK) ok = ok && ktok <= mi[4 * kChunk + e];
+      const float p =
+          ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -mf[e])) : 0.f;
+      const float gt = mf[2 * kChunk + e];
+      pb[r >> 3][r & 7] = (__bf16)(p * gt);
+      dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gt, dp[r], -mf[kChunk + e]));
+    }
+    // dV^T[d][key] += dy^T[d][col] (g P)[col][key];  dK^T[d][key] += Q^T[d][col] dS[col][key]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int db = 0; db < LY::kDB; ++db) {
+        const char* dt = Dst + 16 * t * LY::kRowBytes;
+        const char* qt = Qst + 16 * t * LY::kRowBytes;
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(dt + t_off[db][0], dt + t_off[db][1]),
+                                                         pb[t], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qt + t_off[db][0], qt + t_off[db][1]),
+                                                         dsb[t], dk[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: dK and dV rows of the lane's key at its original token
+  if (!keyvalid) return;
+  char* dkrow = prm.dk + krow * LY::kRowBytes;
+  char* dvrow = prm.dv + krow * LY::kRowBytes;
+  const bool add = prm.accumulate != 0;
+#pragma unroll
+  for (int db = 0; db < LY::kDB; ++db) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * db + 8 * a + 4 * h32;
+      store4(dkrow + 2 * d0, dk[db][4 * a] * prm.scale, dk[db][4 * a + 1] * prm.scale,
+             dk[db][4 * a + 2] * prm.scale, dk[db][4 * a + 3] * prm.scale, add);
+      store4(dvrow + 2 * d0, dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2],
+             dv[db][4 * a + 3], add);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Gate combine of the training forward: out = g_sa * y_sa + g_swa * y_swa, 8 values per thread
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gate_combine_kernel(const char* y_sa, const char* y_swa,
+                                                           const float* gates, char* out,
+                                                           int64_t rows, int gran_per_row) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * gran_per_row) return;
+  const int64_t row = i / gran_per_row;
+  const float ga = gates[row];
+  const float gb = gates[rows + row];
+  const u32x4 a = *(const u32x4*)(y_sa + 16 * i);
+  const u32x4 c = *(const u32x4*)(y_swa + 16 * i);
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[e] = pack2(__builtin_fmaf(ga, bf_lo(a[e]), gb * bf_lo(c[e])),
+                 __builtin_fmaf(ga, bf_hi(a[e]), gb * bf_hi(c[e])));
+  }
+  *(u32x4*)(out + 16 * i) = o;
+}
+
+// ------------------------------------------------------------------------------------------------
+// host-side dispatch
+// ------------------------------------------------------------------------------------------------
+template <typename K>
+static hipError_t launch(K kernel, int nblocks, hipStream_t s, void* e0, void* e1,
+                         const Params& prm) {
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(kernel, dim3(nblocks), dim3(kThreads), 0, s, (hipEvent_t)e0,
+                          (hipEvent_t)e1, 0, prm);
+  else
+    hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kThreads), 0, s, prm);
+  return hipGetLastError();
+}
+
+template <int D, bool PERM, bool SIGMASK>
+static hipError_t launch_t(const BandBwdLaunch& a, Params prm, hipStream_t s) {
+  const int64_t ncols = (int64_t)a.n * prm.G;
+  prm.ntiles = (int)((ncols + kTile - 1) / kTile);
+  prm.nblocks = prm.ntiles * a.B * a.Hkv;
+  hipError_t e = launch(bwd_dq_kernel<D, PERM, SIGMASK>, prm.nblocks, s, a.ev[0], a.ev[1], prm);
+  if (e != hipSuccess) return e;
+  prm.ntiles = (a.n + kTile - 1) / kTile;
+  prm.nblocks = prm.ntiles * a.B * a.Hkv;
+  return launch(bwd_dkdv_kernel<D, PERM, SIGMASK>, prm.nblocks, s, a.ev[2], a.ev[3], prm);
+}
+
+template <int D>
+static hipError_t launch_d(const BandBwdLaunch& a, const Params& prm, hipStream_t s) {
+  if (a.perm)
+    return a.causal ? launch_t<D, true, true>(a, prm, s) : launch_t<D, true, false>(a, prm, s);
+  return launch_t<D, false, false>(a, prm, s);
+}
+
+}  // namespace bwd
+
+hipError_t launch_band_attn_bwd(const BandBwdLaunch& a, hipStream_t stream) {
+  bwd::Params prm;
+  prm.q = (const char*)a.q;
+  prm.k = (const char*)a.k;
+  prm.v = (const char*)a.v;
+  prm.o = (const char*)a.o;
+  prm.dout = (const char*)a.dout;
+  prm.lse = a.lse;
+  prm.gate = a.gate;
+  prm.sigma = a.sigma;
+  prm.dq = (char*)a.dq;
+  prm.dk = (char*)a.dk;
+  prm.dv = (char*)a.dv;
+  prm.dgate = a.dgate;
+  prm.delta = a.delta;
+  prm.B = a.B;
+  prm.n = a.n;
+  prm.Hq = a.Hq;
+  prm.Hkv = a.Hkv;
+  prm.G = a.Hq / a.Hkv;
+  prm.L = a.window - 1;
+  // causal SWA (sigma = identity): no key right of the query
+  prm.R = (!a.perm && a.causal) ? 0 : a.window - 1;
+  prm.scale = (float)(1.0 / __builtin_sqrt((double)a.d));
+  prm.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)a.d));
+  prm.accumulate = a.accumulate ? 1 : 0;
+  prm.ntiles = 0;
+  prm.nblocks = 0;
+  return a.d == 128 ? bwd::launch_d<128>(a, prm, stream) : bwd::launch_d<64>(a, prm, stream);
+}
+
+hipError_t launch_gate_combine(const void* y_sa, const void* y_swa, const float* gates, void* out,
+                               int64_t rows, int d, hipStream_t stream) {
+  const int gpr = d / 8;
+  const int64_t total = rows * gpr;
+  hipLaunchKernelGGL(bwd::gate_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, (const char*)y_sa, (const char*)y_swa, gates, (char*)out, rows, gpr);
+  return hipGetLastError();
+}
+
+}  // namespace ssw

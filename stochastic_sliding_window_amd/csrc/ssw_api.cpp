@@ -1,8 +1,8 @@
 // C ABI of libssw.so (declared in include/ssw.h): argument checking, the host-side permutation
 // generator and dispatch of the gfx950 kernels in band_attn.hip.
 //
-// Nothing here allocates device memory; forward calls only enqueue kernels on the caller's
-// stream.  Errors are reported as negative status codes plus a per-thread message; no C++
+// Nothing here allocates device memory; forward and backward calls only enqueue kernels on the
+// caller's stream.  Errors are reported as negative status codes plus a per-thread message; no C++
 // exception crosses the ABI.
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -210,6 +210,210 @@ int ssw_gated_sa_swa_forward_timed(const void* q, const void* k, const void* v,
   void* const events[4] = {ev_swa_start, ev_swa_end, ev_sa_start, ev_sa_end};
   return gated("ssw_gated_sa_swa_forward_timed", q, k, v, sigma, window, causal, gates, out, B,
                n, Hq, Hkv, d, dtype, stream, events);
+}
+
+// ---- training: forward with the rows' log-sum-exp, backward, gated forward/backward
+
+static int forward_lse(const char* who, const void* q, const void* k, const void* v,
+                       const int32_t* sigma, int window, int causal, void* out, float* lse, int B,
+                       int n, int Hq, int Hkv, int d, int dtype, void* stream) {
+  int st = check_forward(who, q, k, v, out, window, causal, B, n, Hq, Hkv, d, dtype);
+  if (st != SSW_OK || B == 0 || n == 0) return st;
+  if (!lse) return fail(SSW_EINVAL, std::string(who) + ": lse must be non-NULL");
+  if (!aligned(lse, 4) || (sigma && !aligned(sigma, 4)))
+    return fail(SSW_EALIGN, std::string(who) + ": sigma and lse must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (sigma && validate_requested()) {
+    st = check_sigma_on_device(sigma, n, s);
+    if (st != SSW_OK) return st;
+  }
+  ssw::BandLaunch a =
+      make_launch(q, k, v, sigma, window, causal, nullptr, out, B, n, Hq, Hkv, d, dtype);
+  a.lse = lse;
+  return run(who, a, s);
+}
+
+int ssw_sa_forward_lse(const void* q, const void* k, const void* v, const int32_t* sigma,
+                       int window, int causal, void* out, float* lse, int B, int n, int Hq,
+                       int Hkv, int d, int dtype, void* stream) {
+  if (!sigma && B > 0 && n > 0) return fail(SSW_EINVAL, "ssw_sa_forward_lse: sigma must be non-NULL");
+  return forward_lse("ssw_sa_forward_lse", q, k, v, sigma, window, causal, out, lse, B, n, Hq,
+                     Hkv, d, dtype, stream);
+}
+
+int ssw_swa_forward_lse(const void* q, const void* k, const void* v, const int32_t* sigma,
+                        int window, int causal, void* out, float* lse, int B, int n, int Hq,
+                        int Hkv, int d, int dtype, void* stream) {
+  if (sigma) return fail(SSW_EINVAL, "ssw_swa_forward_lse: sigma must be NULL (identity)");
+  return forward_lse("ssw_swa_forward_lse", q, k, v, nullptr, window, causal, out, lse, B, n, Hq,
+                     Hkv, d, dtype, stream);
+}
+
+static int check_backward(const char* who, const void* q, const void* k, const void* v,
+                          const void* o, const void* dout, const float* lse, const void* dq,
+                          const void* dk, const void* dv, const float* delta, int window,
+                          int causal, int B, int n, int Hq, int Hkv, int d, int dtype) {
+  int st = check_forward(who, q, k, v, o, window, causal, B, n, Hq, Hkv, d, dtype);
+  if (st != SSW_OK) return st;
+  if (dtype != SSW_BF16)
+    return fail(SSW_EDTYPE, std::string(who) + ": the backward pass takes bf16 tensors only");
+  if (B == 0 || n == 0) return SSW_OK;
+  if (!dout || !lse || !dq || !dk || !dv || !delta)
+    return fail(SSW_EINVAL, std::string(who) + ": dout, lse, dq, dk, dv and delta must be non-NULL");
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(delta, 4))
+    return fail(SSW_EALIGN, std::string(who) + ": dout, dq, dk, dv must be 16-byte aligned, lse "
+                                               "and delta 4-byte aligned");
+  return SSW_OK;
+}
+
+static ssw::BandBwdLaunch make_bwd(const void* q, const void* k, const void* v,
+                                   const int32_t* sigma, int window, int causal, const float* gate,
+                                   const void* o, const float* lse, const void* dout, void* dq,
+                                   void* dk, void* dv, float* dgate, float* delta, bool accumulate,
+                                   int B, int n, int Hq, int Hkv, int d) {
+  ssw::BandBwdLaunch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.gate = gate;
+  a.sigma = sigma;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dgate = dgate;
+  a.delta = delta;
+  a.B = B;
+  a.n = n;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.window = window < n ? window : n;
+  a.causal = causal != 0;
+  a.perm = sigma != nullptr;
+  a.accumulate = accumulate;
+  return a;
+}
+
+static int run_bwd(const char* who, const ssw::BandBwdLaunch& a, hipStream_t s) {
+  hipError_t e = ssw::launch_band_attn_bwd(a, s);
+  if (e != hipSuccess)
+    return fail(SSW_EHIP, std::string(who) + ": kernel launch failed: " + hipGetErrorString(e));
+  return SSW_OK;
+}
+
+static int backward(const char* who, const void* q, const void* k, const void* v,
+                    const int32_t* sigma, int window, int causal, const float* gate, const void* out,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dgate,
+                    float* delta, int accumulate, int B, int n, int Hq, int Hkv, int d, int dtype,
+                    void* stream) {
+  int st = check_backward(who, q, k, v, out, dout, lse, dq, dk, dv, delta, window, causal, B, n,
+                          Hq, Hkv, d, dtype);
+  if (st != SSW_OK || B == 0 || n == 0) return st;
+  if (accumulate != 0 && accumulate != 1)
+    return fail(SSW_EINVAL, std::string(who) + ": accumulate must be 0 or 1");
+  if ((gate && !aligned(gate, 4)) || (dgate && !aligned(dgate, 4)) || (sigma && !aligned(sigma, 4)))
+    return fail(SSW_EALIGN, std::string(who) + ": sigma, gate and dgate must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (sigma && validate_requested()) {
+    st = check_sigma_on_device(sigma, n, s);
+    if (st != SSW_OK) return st;
+  }
+  return run_bwd(who, make_bwd(q, k, v, sigma, window, causal, gate, out, lse, dout, dq, dk, dv,
+                               dgate, delta, accumulate != 0, B, n, Hq, Hkv, d),
+                 s);
+}
+
+int ssw_sa_backward(const void* q, const void* k, const void* v, const int32_t* sigma, int window,
+                    int causal, const float* gate, const void* out, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, float* dgate, float* delta,
+                    int accumulate, int B, int n, int Hq, int Hkv, int d, int dtype, void* stream) {
+  if (!sigma && B > 0 && n > 0) return fail(SSW_EINVAL, "ssw_sa_backward: sigma must be non-NULL");
+  return backward("ssw_sa_backward", q, k, v, sigma, window, causal, gate, out, lse, dout, dq, dk,
+                  dv, dgate, delta, accumulate, B, n, Hq, Hkv, d, dtype, stream);
+}
+
+int ssw_swa_backward(const void* q, const void* k, const void* v, const int32_t* sigma,
+                     int window, int causal, const float* gate, const void* out, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, float* dgate, float* delta,
+                     int accumulate, int B, int n, int Hq, int Hkv, int d, int dtype,
+                     void* stream) {
+  if (sigma) return fail(SSW_EINVAL, "ssw_swa_backward: sigma must be NULL (identity)");
+  return backward("ssw_swa_backward", q, k, v, nullptr, window, causal, gate, out, lse, dout, dq,
+                  dk, dv, dgate, delta, accumulate, B, n, Hq, Hkv, d, dtype, stream);
+}
+
+int ssw_gated_sa_swa_forward_train(const void* q, const void* k, const void* v,
+                                   const int32_t* sigma, int window, int causal,
+                                   const float* gates, void* out, void* y_sa, float* lse_sa,
+                                   void* y_swa, float* lse_swa, int B, int n, int Hq, int Hkv,
+                                   int d, int dtype, void* stream) {
+  const char* who = "ssw_gated_sa_swa_forward_train";
+  int st = check_forward(who, q, k, v, out, window, causal, B, n, Hq, Hkv, d, dtype);
+  if (st != SSW_OK) return st;
+  if (dtype != SSW_BF16)
+    return fail(SSW_EDTYPE, "ssw_gated_sa_swa_forward_train: bf16 tensors only");
+  if (B == 0 || n == 0) return SSW_OK;
+  if (!sigma || !gates || !y_sa || !lse_sa || !y_swa || !lse_swa)
+    return fail(SSW_EINVAL, std::string(who) + ": sigma, gates, y_sa, lse_sa, y_swa and lse_swa "
+                                               "must be non-NULL");
+  if (!aligned(y_sa, 16) || !aligned(y_swa, 16) || !aligned(gates, 4) || !aligned(sigma, 4) ||
+      !aligned(lse_sa, 4) || !aligned(lse_swa, 4))
+    return fail(SSW_EALIGN, std::string(who) + ": y_sa and y_swa must be 16-byte aligned, sigma, "
+                                               "gates and the lse buffers 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_requested()) {
+    st = check_sigma_on_device(sigma, n, s);
+    if (st != SSW_OK) return st;
+  }
+  ssw::BandLaunch a1 =
+      make_launch(q, k, v, nullptr, window, causal, nullptr, y_swa, B, n, Hq, Hkv, d, dtype);
+  a1.lse = lse_swa;
+  ssw::BandLaunch a2 =
+      make_launch(q, k, v, sigma, window, causal, nullptr, y_sa, B, n, Hq, Hkv, d, dtype);
+  a2.lse = lse_sa;
+  if ((st = run(who, a1, s)) != SSW_OK) return st;
+  if ((st = run(who, a2, s)) != SSW_OK) return st;
+  hipError_t e = ssw::launch_gate_combine(y_sa, y_swa, gates, out, (int64_t)B * n * Hq, d, s);
+  if (e != hipSuccess)
+    return fail(SSW_EHIP, std::string(who) + ": kernel launch failed: " + hipGetErrorString(e));
+  return SSW_OK;
+}
+
+int ssw_gated_sa_swa_backward(const void* q, const void* k, const void* v, const int32_t* sigma,
+                              int window, int causal, const float* gates, const void* y_sa,
+                              const float* lse_sa, const void* y_swa, const float* lse_swa,
+                              const void* dout, void* dq, void* dk, void* dv, float* dgates,
+                              float* delta, int B, int n, int Hq, int Hkv, int d, int dtype,
+                              void* stream) {
+  const char* who = "ssw_gated_sa_swa_backward";
+  int st = check_backward(who, q, k, v, y_sa, dout, lse_sa, dq, dk, dv, delta, window, causal, B,
+                          n, Hq, Hkv, d, dtype);
+  if (st != SSW_OK || B == 0 || n == 0) return st;
+  if (!sigma || !gates || !y_swa || !lse_swa)
+    return fail(SSW_EINVAL, std::string(who) + ": sigma, gates, y_swa and lse_swa must be non-NULL");
+  if (!aligned(y_swa, 16) || !aligned(gates, 4) || !aligned(sigma, 4) || !aligned(lse_swa, 4) ||
+      (dgates && !aligned(dgates, 4)))
+    return fail(SSW_EALIGN, std::string(who) + ": y_swa must be 16-byte aligned, sigma, gates, "
+                                               "lse_swa and dgates 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_requested()) {
+    st = check_sigma_on_device(sigma, n, s);
+    if (st != SSW_OK) return st;
+  }
+  const size_t plane = (size_t)B * n * Hq;
+  // SA path first (writes the gradients), then the SWA path (adds to them); each pass's Delta
+  // is consumed by its own dK/dV kernel before the next pass overwrites it (stream order)
+  ssw::BandBwdLaunch a1 = make_bwd(q, k, v, sigma, window, causal, gates, y_sa, lse_sa, dout, dq,
+                                   dk, dv, dgates, delta, false, B, n, Hq, Hkv, d);
+  ssw::BandBwdLaunch a2 =
+      make_bwd(q, k, v, nullptr, window, causal, gates + plane, y_swa, lse_swa, dout, dq, dk, dv,
+               dgates ? dgates + plane : nullptr, delta, true, B, n, Hq, Hkv, d);
+  if ((st = run_bwd(who, a1, s)) != SSW_OK) return st;
+  return run_bwd(who, a2, s);
 }
 
 int ssw_make_permutation(uint64_t seed, int n, int32_t* sigma_out, int32_t* inv_out) {

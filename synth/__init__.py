@@ -88,3 +88,13 @@ def gates(seed: int, B: int, n: int, Hq: int):
     """Gate values float32 [2, B, n, Hq] (g_sa first), each sigmoid(N(0, 1))."""
     g = torch.Generator().manual_seed(seed ^ 0x5A5A)
     return torch.sigmoid(torch.randn(2, B, n, Hq, generator=g, dtype=torch.float32))
+
+
+def upstream_grad(seed: int, B: int, n: int, Hq: int, d: int, dtype: str = "bf16"):
+    """An upstream gradient dL/dY [B, n, Hq, d], N(0, 1), cast to ``dtype`` (CPU tensor).
+
+    Stands in for whatever the layers above would send back; the backward's cost and numerics do
+    not depend on its distribution beyond its scale.
+    """
+    g = torch.Generator().manual_seed(seed ^ 0x3C3C)
+    return torch.randn(B, n, Hq, d, generator=g, dtype=torch.float32).to(_DT[dtype])

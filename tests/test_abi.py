@@ -157,3 +157,83 @@ def test_one_hip_runtime_in_process():
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert res.returncode == 0, res.stderr
     assert res.stdout.strip().splitlines()[-1] == "1"
+
+
+# ---- training entry points: argument checks (no HIP call is reached) ---------------------------
+
+_VP, _I = ctypes.c_void_p, ctypes.c_int
+for _n in ("ssw_sa_forward_lse", "ssw_swa_forward_lse"):
+    getattr(_lib, _n).argtypes = [_VP] * 4 + [_I] * 2 + [_VP] * 2 + [_I] * 6 + [_VP]
+    getattr(_lib, _n).restype = _I
+for _n in ("ssw_sa_backward", "ssw_swa_backward"):
+    getattr(_lib, _n).argtypes = [_VP] * 4 + [_I] * 2 + [_VP] * 9 + [_I] * 7 + [_VP]
+    getattr(_lib, _n).restype = _I
+_lib.ssw_gated_sa_swa_forward_train.argtypes = [_VP] * 4 + [_I] * 2 + [_VP] * 6 + [_I] * 6 + [_VP]
+_lib.ssw_gated_sa_swa_forward_train.restype = _I
+_lib.ssw_gated_sa_swa_backward.argtypes = [_VP] * 4 + [_I] * 2 + [_VP] * 11 + [_I] * 6 + [_VP]
+_lib.ssw_gated_sa_swa_backward.restype = _I
+
+BWD_GOOD = dict(GOOD, out=P, lse=P, dout=P, dq=P, dk=P, dv=P, dgate=None, delta=P, accumulate=0)
+
+
+def _call_bwd(fn, **kw):
+    a = dict(BWD_GOOD)
+    if fn == "ssw_swa_backward":
+        a["sigma"] = None
+    a.update(kw)
+    return getattr(_lib, fn)(a["q"], a["k"], a["v"], a["sigma"], a["window"], a["causal"],
+                             a["gate"], a["out"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                             a["dgate"], a["delta"], a["accumulate"], a["B"], a["n"], a["Hq"],
+                             a["Hkv"], a["d"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("fn", ["ssw_sa_backward", "ssw_swa_backward"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=0), -1),
+    (dict(causal=3), -1),
+    (dict(accumulate=2), -1),
+    (dict(dout=None), -1),
+    (dict(lse=None), -1),
+    (dict(delta=None), -1),
+    (dict(dk=None), -1),
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(dtype=0), -3),           # the backward takes bf16 only
+    (dict(d=80), -3),
+    (dict(dq=P + 8), -4),
+    (dict(lse=P + 2), -4),
+    (dict(gate=P + 1), -4),
+])
+def test_backward_bad_arguments_rejected(fn, kw, status):
+    assert _call_bwd(fn, **kw) == status
+    assert _lib.ssw_last_error().decode().startswith(fn)
+
+
+def test_backward_entry_point_specific_checks():
+    assert _call_bwd("ssw_sa_backward", sigma=None) == -1
+    assert _call_bwd("ssw_swa_backward", sigma=P) == -1
+    assert _call_bwd("ssw_sa_backward", B=0, q=None, k=None, v=None, out=None) == 0
+
+
+def test_forward_lse_checks():
+    args = lambda sig, lse, dtype=1: (P, P, P, sig, 8, 1, P, lse, 1, 64, 4, 2, 64, dtype, None)
+    assert _lib.ssw_sa_forward_lse(*args(None, P)) == -1
+    assert _lib.ssw_sa_forward_lse(*args(P, None)) == -1
+    assert _lib.ssw_sa_forward_lse(*args(P, P + 2)) == -4
+    assert _lib.ssw_swa_forward_lse(*args(P, P)) == -1
+
+
+def test_gated_training_checks():
+    fwd = lambda **kw: _lib.ssw_gated_sa_swa_forward_train(
+        P, P, P, kw.get("sigma", P), 8, 1, kw.get("gates", P), P, kw.get("y_sa", P), P, P, P,
+        1, 64, 4, 2, 64, kw.get("dtype", 1), None)
+    assert fwd(gates=None) == -1
+    assert fwd(y_sa=None) == -1
+    assert fwd(y_sa=P + 8) == -4
+    assert fwd(dtype=0) == -3
+    bwd = lambda **kw: _lib.ssw_gated_sa_swa_backward(
+        P, P, P, kw.get("sigma", P), 8, 1, P, P, P, kw.get("y_swa", P), P, P, P, P, P,
+        kw.get("dgates", None), P, 1, 64, 4, 2, 64, kw.get("dtype", 1), None)
+    assert bwd(sigma=None) == -1
+    assert bwd(y_swa=None) == -1
+    assert bwd(dgates=P + 1) == -4
+    assert bwd(dtype=0) == -3
