@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu-baseline]
     python bench.py --nsweep      (SA against full causal attention, n = 2K .. 32K)
+    python bench.py --train       (gated layer training step: forward with lse + backward)
 
 One step is one pass of the whole hot path over one layer's synthetic input: one call of
 ssw_gated_sa_swa_forward, i.e. the SWA pass (leaves g_swa * Y_swa as the intermediate) followed by
@@ -67,6 +68,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size (0 = auto)")
     ap.add_argument("--nsweep", action="store_true",
                     help="instead: SA (w = --window) against full causal attention for n = 2K..32K")
+    ap.add_argument("--train", action="store_true",
+                    help="instead: the gated layer's training step (forward with lse + backward)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -82,6 +85,8 @@ def main():
 
     if args.nsweep:
         return nsweep(args)
+    if args.train:
+        return train(args)
 
     wl = synth.workload(4)
     B, n, Hq, Hkv, d = wl.B, wl.n, wl.Hq, wl.Hkv, wl.d
@@ -267,6 +272,113 @@ def nsweep(args):
             "config": {"workload": "long-context layer shape, n sweep", "B": B, "Hq": Hq,
                        "Hkv": Hkv, "d": d, "window": w, "causal": True},
             "sweep": rows}
+    print(json.dumps(line), flush=True)
+
+
+def train(args):
+    """The gated layer's training step at the long-context workload (B 1, n 32768, 32 / 8 heads,
+    d 128, bf16, causal, w = --window): ssw_gated_sa_swa_forward_train (SWA and SA passes with
+    lse, gate combine) then ssw_gated_sa_swa_backward (dQ and dK/dV kernels for each path).
+    Also times the backward alone and each path's backward alone.  One JSON line."""
+    import numpy as np
+    import torch
+
+    import stochastic_sliding_window_amd as ssw
+    import synth
+
+    wl = synth.workload(4)
+    B, n, Hq, Hkv, d = wl.B, wl.n, wl.Hq, wl.Hkv, wl.d
+    w = args.window
+    causal = True
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    seed = synth.data_seed(4, 0)
+    q, k, v = synth.qkv(seed, B, n, Hq, Hkv, d, wl.dtype)
+    g = synth.gates(seed, B, n, Hq)
+    dy = synth.upstream_grad(seed, B, n, Hq, d, wl.dtype)
+    sigma = ssw.make_permutation(synth.sigma_seed(4, 0), n)
+    ROT = 2
+    sets = []
+    for _ in range(ROT):
+        s = dict(q=q.to(dev), k=k.to(dev), v=v.to(dev), g=g.to(dev), dy=dy.to(dev),
+                 sigma=torch.from_numpy(sigma).to(dev), out=torch.empty(B, n, Hq, d, dtype=q.dtype,
+                                                                        device=dev))
+        s["saved"] = ssw.gated_sa_swa_forward_train(s["q"], s["k"], s["v"], s["sigma"], w, causal,
+                                                    s["g"], out=s["out"])[1]
+        s["grads"] = ssw.gated_sa_swa_backward(s["q"], s["k"], s["v"], s["sigma"], w, causal,
+                                               s["g"], s["saved"], s["dy"])
+        s["delta"] = torch.empty(B, n, Hq, dtype=torch.float32, device=dev)
+        sets.append(s)
+    torch.cuda.synchronize()
+
+    def fwd(s):
+        ssw.gated_sa_swa_forward_train(s["q"], s["k"], s["v"], s["sigma"], w, causal, s["g"],
+                                       out=s["out"], saved=s["saved"])
+
+    def bwd(s):
+        dq, dk, dv, dg = s["grads"]
+        ssw.gated_sa_swa_backward(s["q"], s["k"], s["v"], s["sigma"], w, causal, s["g"],
+                                  s["saved"], s["dy"], dq=dq, dk=dk, dv=dv, dgates=dg,
+                                  delta=s["delta"])
+
+    def path_bwd(s, sa):
+        dq, dk, dv, dg = s["grads"]
+        y_sa, lse_sa, y_swa, lse_swa = s["saved"]
+        if sa:
+            ssw.sa_backward(s["q"], s["k"], s["v"], s["sigma"], w, causal, y_sa, lse_sa, s["dy"],
+                            gate=s["g"][0], dq=dq, dk=dk, dv=dv, dgate=dg[0], delta=s["delta"])
+        else:
+            ssw.swa_backward(s["q"], s["k"], s["v"], w, causal, y_swa, lse_swa, s["dy"],
+                             gate=s["g"][1], dq=dq, dk=dk, dv=dv, dgate=dg[1], delta=s["delta"])
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, K, W):
+        for i in range(W):
+            fn(sets[i % ROT])
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(K):
+            fn(sets[i % ROT])
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / K
+
+    K, W = args.steps, args.warmup
+    step_ms = timed(lambda s: (fwd(s), bwd(s)), K, W)
+    fwd_ms = timed(fwd, K, W)
+    bwd_ms = timed(bwd, K, W)
+    sa_bwd_ms = timed(lambda s: path_bwd(s, True), K, W)
+    swa_bwd_ms = timed(lambda s: path_bwd(s, False), K, W)
+
+    pairs = causal_pairs(n, w)
+    fwd_flops = 2 * 4 * d * B * Hq * pairs          # two paths, QK^T and PV
+    bwd_flops = 2 * 10 * d * B * Hq * pairs         # two paths, S, dP, dV, dK, dQ
+    e = 2
+    big, small, rows = B * n * Hq * d * e, B * n * Hkv * d * e, B * n * Hq * 4
+    # one path's backward: q, k, v, A, dy, lse, gate (+ sigma) read; dq, dk, dv, dgate written
+    path_bytes = 3 * big + 2 * small + 2 * rows + big + 2 * small + rows
+    bwd_bytes = 2 * path_bytes + big + 2 * small     # the second path adds to dq, dk, dv
+    tokens = B * n
+    line = {
+        "metric": "gated SA+SWA training step (fwd with lse + bwd) tokens/s at n=32K, w=128 (1 GPU)",
+        "value": round(tokens / (step_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic: Q,K,V,dY ~ N(0,1), gates sigmoid(N(0,1)), seeded sigma",
+        "config": {"workload": f"{wl.name} gated SA+SWA training step", "B": B, "n": n, "Hq": Hq,
+                   "Hkv": Hkv, "d": d, "window": w, "causal": causal},
+        "fwd_train_us": round(fwd_ms * 1e3, 1), "bwd_us": round(bwd_ms * 1e3, 1),
+        "sa_bwd_us": round(sa_bwd_ms * 1e3, 1), "swa_bwd_us": round(swa_bwd_ms * 1e3, 1),
+        "step_tflops": round((fwd_flops + bwd_flops) / (step_ms * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1),
+        "bwd_algorithmic_bytes": bwd_bytes,
+        "bwd_hbm_gbs": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
+    }
+    log(f"training step {step_ms * 1e3:.1f} us: forward {fwd_ms * 1e3:.1f} us, backward "
+        f"{bwd_ms * 1e3:.1f} us (SA path {sa_bwd_ms * 1e3:.1f}, SWA path {swa_bwd_ms * 1e3:.1f}); "
+        f"backward {line['bwd_tflops']} TFLOP/s, {line['bwd_hbm_gbs']} GB/s algorithmic")
     print(json.dumps(line), flush=True)
 
 

@@ -47,6 +47,9 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kChunk = 32;     // keys (dq kernel) or query columns (dk/dv kernel) per chunk
 constexpr int kTile = 128;     // columns (dq kernel) or key slots (dk/dv kernel) per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+// sigma entries held in LDS at a time: the chunk loads read a row's original index there, so a
+// chunk's row loads wait for one memory latency instead of two (sigma, then the row)
+constexpr int kSigCap = 2048;
 
 struct Params {
   const char* q;
@@ -66,6 +69,7 @@ struct Params {
   int L, R;          // band: key slots [p - L, p + R] of query slot p
   float scale_log2;  // log2(e) / sqrt(d)
   float scale;       // 1 / sqrt(d)
+  float inv_g;       // 1 / G
   int ntiles;        // tiles per (batch row, KV head)
   int nblocks;       // ntiles * B * Hkv
   int accumulate;
@@ -163,6 +167,12 @@ __device__ __forceinline__ bf16x8 tr_read(const char* lo_p, const char* hi_p) {
   return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
 }
 
+// floor(x / G) for 0 <= x < 2^12 with inv_g = 1/G in fp32: (x + 1/2) / G lies at least 1/(2G)
+// from every integer, far beyond the rounding error of the product
+__device__ __forceinline__ int div_small(int x, float inv_g) {
+  return (int)(((float)x + 0.5f) * inv_g);
+}
+
 __device__ __forceinline__ bf16x8 ld_bf16x8(const char* p) {
   return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
 }
@@ -175,7 +185,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void bwd_dq_kernel(Params prm) {
   using LY = Lay<D>;
   constexpr int kStage = 2 * LY::kMat + kChunk * 4;  // K, V, sigma of the chunk's keys
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  constexpr int kSigOff = 2 * kStage;
+  constexpr int kSegChunks = kSigCap / kChunk;        // chunks whose keys' sigma fit in LDS
+  __shared__ __attribute__((aligned(16))) char smem[kSigOff + (PERM ? kSigCap * 4 : 0)];
+  int* sig_lds = (int*)(smem + kSigOff);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -244,6 +257,17 @@ void bwd_dq_kernel(Params prm) {
     if (prm.dgate) prm.dgate[rowq] = dot;
   }
 
+  // ---- sigma of the keys of chunks [seg_c0, seg_c0 + kSegChunks), in LDS (permuted operator)
+  int seg_c0 = 0;
+  auto load_sigma_seg = [&](int c0) {
+    const int key0 = kbeg + c0 * kChunk;
+    for (int i = tid; i < kSigCap; i += kThreads) {
+      const int key = key0 + i;
+      sig_lds[i] = key < n ? prm.sigma[key] : INT_MAX;
+    }
+  };
+  auto orig_of_key = [&](int key) { return PERM ? sig_lds[key - kbeg - seg_c0 * kChunk] : key; };
+
   // ---- chunk staging: this thread's granules of the chunk's K and V rows, one chunk ahead
   u32x4 st_regs[LY::kPer];
   int st_sig = 0;
@@ -256,19 +280,15 @@ void bwd_dq_kernel(Params prm) {
       const int rem = gi - mat * (kChunk * LY::kGran);
       const int row = rem / LY::kGran;
       const int gran = rem - row * LY::kGran;
-      const int key = kc0 + rho(row);
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (key < n) {
-        const int tok = PERM ? prm.sigma[key] : key;
-        const char* src = (mat ? prm.v : prm.k) +
-                          ((((int64_t)b * n + tok) * prm.Hkv + g) * D + gran * 8) * 2;
-        val = *(const u32x4*)src;
-      }
-      st_regs[i] = val;
+      // keys past the end load the last key's rows (finite values; the band test drops them)
+      const int key = min(kc0 + rho(row), n - 1);
+      const int tok = orig_of_key(key);
+      st_regs[i] = *(const u32x4*)((mat ? prm.v : prm.k) +
+                                   ((((int64_t)b * n + tok) * prm.Hkv + g) * D + gran * 8) * 2);
     }
     if (tid < kChunk) {
       const int key = kc0 + tid;
-      st_sig = key < n ? (PERM ? prm.sigma[key] : key) : INT_MAX;
+      st_sig = key < n ? orig_of_key(key) : INT_MAX;
     }
   };
   auto store_chunk = [&](int st) {
@@ -299,13 +319,25 @@ void bwd_dq_kernel(Params prm) {
 #pragma unroll
   for (int db = 0; db < LY::kDB; ++db) acc[db] = zero16();
 
+  if constexpr (PERM) {
+    load_sigma_seg(0);
+    __syncthreads();
+  }
   load_chunk(0);
   for (int c = 0; c < nchunks; ++c) {
     const int st = c & 1;
     // stage st was last read in iteration c - 2, before every wave passed barrier c - 1
     store_chunk(st);
     __syncthreads();
-    if (c + 1 < nchunks) load_chunk(c + 1);
+    if (c + 1 < nchunks) {
+      if (PERM && c + 1 - seg_c0 >= kSegChunks) {
+        // every thread's sigma reads for chunk c were done before its store_chunk above
+        seg_c0 = c + 1;
+        load_sigma_seg(seg_c0);
+        __syncthreads();
+      }
+      load_chunk(c + 1);
+    }
     if (!wave_on || c < c_first || c > c_last) continue;
     const char* Kst = smem + st * kStage;
     const char* Vst = Kst + LY::kMat;
@@ -361,20 +393,20 @@ void bwd_dq_kernel(Params prm) {
 // ------------------------------------------------------------------------------------------------
 // dK, dV: key-major
 // ------------------------------------------------------------------------------------------------
-// At d = 128 the K/V operands and the two accumulators alone take 192 registers per lane, so
-// the kernel is sized for one wave per SIMD (up to 512 registers, no spills).
-template <int D>
-constexpr int kDkdvWaves = D >= 128 ? 1 : 2;
-
+// The V rows of the workgroup's keys sit in LDS rather than in registers: the K operand and the
+// two accumulators already take 160 registers per lane at d = 128, and two waves per SIMD need
+// the total to stay within 256.
 template <int D, bool PERM, bool SIGMASK>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kDkdvWaves<D>, kDkdvWaves<D>)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(Params prm) {
   using LY = Lay<D>;
   // per stage: Q rows, dy rows, then per column log2-domain lse, Delta, gate, slot, original index
   constexpr int kMetaOff = 2 * LY::kMat;
   constexpr int kStage = kMetaOff + 5 * kChunk * 4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  constexpr int kVOff = 2 * kStage;                      // V rows of the 128 keys
+  constexpr int kSigOff = kVOff + kTile * LY::kRowBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSigOff + (PERM ? kSigCap * 4 : 0)];
+  int* sig_lds = (int*)(smem + kSigOff);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -411,15 +443,28 @@ void bwd_dkdv_kernel(Params prm) {
   const int c_first = (max(0, wk_lo - R) * G - col_lo) / kChunk;
   const int c_last = (min(n - 1, wk_hi + L) * G + G - 1 - col_lo) / kChunk;
 
-  // ---- K and V rows of the lane's key as B operands (k step kb holds d = 16kb + 8h32 + [0, 8))
+  // ---- K row of the lane's key as B operands (k step kb holds d = 16kb + 8h32 + [0, 8)); its V
+  // row goes to LDS in the same swizzled layout as the stage matrices (row = key within the tile)
   const int64_t krow = ((int64_t)b * n + ktok) * prm.Hkv + g;
-  bf16x8 kf[LY::kKB], vf[LY::kKB];
+  bf16x8 kf[LY::kKB];
+  char* vrows = smem + kVOff + wave * 32 * LY::kRowBytes;
 #pragma unroll
   for (int kb = 0; kb < LY::kKB; ++kb) {
     const int off = (16 * kb + 8 * h32) * 2;
     kf[kb] = ld_bf16x8(prm.k + krow * LY::kRowBytes + off);
-    vf[kb] = ld_bf16x8(prm.v + krow * LY::kRowBytes + off);
+    *(u32x4*)(vrows + gran_off<D>(r32, 2 * kb + h32)) =
+        *(const u32x4*)(prm.v + krow * LY::kRowBytes + off);
   }
+
+  // ---- sigma of the query slots [seg_s0, seg_s0 + kSigCap), in LDS (permuted operator)
+  int seg_s0 = col_lo / G;
+  auto load_sigma_seg = [&](int s0) {
+    for (int i = tid; i < kSigCap; i += kThreads) {
+      const int slot = s0 + i;
+      sig_lds[i] = slot < n ? prm.sigma[slot] : 0;
+    }
+  };
+  auto orig_of_slot = [&](int slot) { return PERM ? sig_lds[slot - seg_s0] : slot; };
 
   // ---- chunk staging: Q and dy rows of 32 query columns plus their per-column values
   u32x4 st_regs[LY::kPer];
@@ -427,6 +472,8 @@ void bwd_dkdv_kernel(Params prm) {
   int m_slot = 0, m_orig = 0;
   auto load_chunk = [&](int c) {
     const int c0 = col_lo + c * kChunk;
+    const int slot0 = c0 / G;  // wave-uniform
+    const int rem0 = c0 - slot0 * G;
 #pragma unroll
     for (int i = 0; i < LY::kPer; ++i) {
       const int gi = i * kThreads + tid;
@@ -434,24 +481,22 @@ void bwd_dkdv_kernel(Params prm) {
       const int rem = gi - mat * (kChunk * LY::kGran);
       const int row = rem / LY::kGran;
       const int gran = rem - row * LY::kGran;
-      const int col = c0 + rho(row);
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (col < nG) {
-        const int slot = col / G;
-        const int tok = PERM ? prm.sigma[slot] : slot;
-        const char* src = (mat ? prm.dout : prm.q) +
-                          ((((int64_t)b * n + tok) * prm.Hq + g * G + (col - slot * G)) * D +
-                           gran * 8) * 2;
-        val = *(const u32x4*)src;
-      }
-      st_regs[i] = val;
+      // columns past the end load the last column's rows (finite values; their band test fails)
+      const int x = min(rem0 + rho(row), nG - 1 - slot0 * G);
+      const int ds = div_small(x, prm.inv_g);
+      const int tok = orig_of_slot(slot0 + ds);
+      st_regs[i] = *(const u32x4*)((mat ? prm.dout : prm.q) +
+                                   ((((int64_t)b * n + tok) * prm.Hq + g * G + (x - ds * G)) * D +
+                                    gran * 8) * 2);
     }
     if (tid < kChunk) {
       const int col = c0 + tid;
       if (col < nG) {
-        const int slot = col / G;
-        const int tok = PERM ? prm.sigma[slot] : slot;
-        const int64_t row = ((int64_t)b * n + tok) * prm.Hq + g * G + (col - slot * G);
+        const int x = rem0 + tid;
+        const int ds = div_small(x, prm.inv_g);
+        const int slot = slot0 + ds;
+        const int tok = orig_of_slot(slot);
+        const int64_t row = ((int64_t)b * n + tok) * prm.Hq + g * G + (x - ds * G);
         m_lse2 = prm.lse[row] * kLog2e;
         m_delta = prm.delta[row];
         m_gate = prm.gate ? prm.gate[row] : 1.0f;
@@ -506,12 +551,25 @@ void bwd_dkdv_kernel(Params prm) {
     dv[db] = zero16();
   }
 
+  if constexpr (PERM) {
+    load_sigma_seg(seg_s0);
+    __syncthreads();
+  }
   load_chunk(0);
   for (int c = 0; c < nchunks; ++c) {
     const int st = c & 1;
     store_chunk(st);
     __syncthreads();
-    if (c + 1 < nchunks) load_chunk(c + 1);
+    if (c + 1 < nchunks) {
+      const int last_slot = min(n - 1, (col_lo + (c + 2) * kChunk - 1) / G);
+      if (PERM && last_slot - seg_s0 >= kSigCap) {
+        // every thread's sigma reads for chunk c were done before its store_chunk above
+        seg_s0 = (col_lo + (c + 1) * kChunk) / G;
+        load_sigma_seg(seg_s0);
+        __syncthreads();
+      }
+      load_chunk(c + 1);
+    }
     if (!wave_on || c < c_first || c > c_last) continue;
     const char* Qst = smem + st * kStage;
     const char* Dst = Qst + LY::kMat;
@@ -525,7 +583,8 @@ void bwd_dkdv_kernel(Params prm) {
 #pragma unroll
     for (int kb = 0; kb < LY::kKB; ++kb) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Qst + a_off[kb]), kf[kb], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Dst + a_off[kb]), vf[kb], dp, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Dst + a_off[kb]),
+                                                   ld_bf16x8(vrows + a_off[kb]), dp, 0, 0, 0);
     }
     bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -654,6 +713,7 @@ hipError_t launch_band_attn_bwd(const BandBwdLaunch& a, hipStream_t stream) {
   // causal SWA (sigma = identity): no key right of the query
   prm.R = (!a.perm && a.causal) ? 0 : a.window - 1;
   prm.scale = (float)(1.0 / __builtin_sqrt((double)a.d));
+  prm.inv_g = 1.0f / (float)prm.G;
   prm.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)a.d));
   prm.accumulate = a.accumulate ? 1 : 0;
   prm.ntiles = 0;
