@@ -15,6 +15,7 @@ definitions on the pages:
   formulation of SA used to cross-check the first.
 * backward.py    -- the gradients of those forwards (chain rule through the definition, one
   query row at a time), the rows' log-sum-exp, and sampled-row forms for large n.
+* decode.py      -- one decode step over a KV cache (row t of causal SA over the full context).
 
 Sources (the pages):
   [SA-ja] "技術的概要：確率的アテンション" (gist.science/ja/paper/2604.00754) -- Stochastic
@@ -49,6 +50,7 @@ from .backward import (
     attention_backward_key_rows,
     attending_queries,
 )
+from .decode import sa_decode, swa_decode, gated_decode
 
 __all__ = [
     "splitmix64_stream",
@@ -69,4 +71,7 @@ __all__ = [
     "attention_backward_query_rows",
     "attention_backward_key_rows",
     "attending_queries",
+    "sa_decode",
+    "swa_decode",
+    "gated_decode",
 ]
