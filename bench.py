@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu-baseline]
     python bench.py --nsweep      (SA against full causal attention, n = 2K .. 32K)
     python bench.py --train       (gated layer training step: forward with lse + backward)
+    python bench.py --decode      (gated decode step over a KV cache, batch 128, n_max 32768)
 
 One step is one pass of the whole hot path over one layer's synthetic input: one call of
 ssw_gated_sa_swa_forward, i.e. the SWA pass (leaves g_swa * Y_swa as the intermediate) followed by
@@ -70,6 +71,9 @@ def main():
                     help="instead: SA (w = --window) against full causal attention for n = 2K..32K")
     ap.add_argument("--train", action="store_true",
                     help="instead: the gated layer's training step (forward with lse + backward)")
+    ap.add_argument("--decode", action="store_true",
+                    help="instead: one gated decode step per batch row over a KV cache")
+    ap.add_argument("--batch", type=int, default=128, help="decode batch rows")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -87,6 +91,8 @@ def main():
         return nsweep(args)
     if args.train:
         return train(args)
+    if args.decode:
+        return decode(args)
 
     wl = synth.workload(4)
     B, n, Hq, Hkv, d = wl.B, wl.n, wl.Hq, wl.Hkv, wl.d
@@ -379,6 +385,97 @@ def train(args):
     log(f"training step {step_ms * 1e3:.1f} us: forward {fwd_ms * 1e3:.1f} us, backward "
         f"{bwd_ms * 1e3:.1f} us (SA path {sa_bwd_ms * 1e3:.1f}, SWA path {swa_bwd_ms * 1e3:.1f}); "
         f"backward {line['bwd_tflops']} TFLOP/s, {line['bwd_hbm_gbs']} GB/s algorithmic")
+    print(json.dumps(line), flush=True)
+
+
+def decode(args):
+    """One gated decode step per batch row (ssw_gated_sa_swa_decode) over a KV cache of the
+    long-context layer shape (32 query / 8 KV heads, d 128, bf16), n_max 32768, w = --window,
+    batch --batch, positions drawn uniformly in [n_max / 2, n_max).  Also SA and SWA steps alone.
+    The roofline counts the K/V rows each step must read: the SA neighbours (tokens <= t in the
+    band of sigma^-1(t)) and the SWA window, plus q, out and the gates."""
+    import numpy as np
+    import torch
+
+    import stochastic_sliding_window_amd as ssw
+    import synth
+
+    B, n, Hq, Hkv, d, w = args.batch, 32768, 32, 8, 128, args.window
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    seed = synth.data_seed(4, 0)
+    rng = np.random.default_rng(seed)
+    pos = rng.integers(n // 2, n, size=B).astype(np.int32)
+    # the new tokens' queries; eight distinct caches drawn on the host, copied round-robin into
+    # the B batch rows' own cache buffers on the device (each row still reads its own memory)
+    q = synth.qkv(seed, B, 1, Hq, Hkv, d, "bf16")[0][:, 0].contiguous()
+    kd = torch.empty(B, n, Hkv, d, dtype=torch.bfloat16, device=dev)
+    vd = torch.empty_like(kd)
+    for i in range(min(B, 8)):
+        _, kb, vb = synth.qkv(seed + 1 + i, 1, n, 1, Hkv, d, "bf16")
+        kb, vb = kb[0].to(dev), vb[0].to(dev)
+        for b in range(i, B, 8):
+            kd[b].copy_(kb)
+            vd[b].copy_(vb)
+    log(f"decode caches ready: {B} rows of {n} positions")
+    g = synth.gates(seed, B, 1, Hq)[:, :, 0].contiguous()
+    sig, inv = ssw.make_permutation(synth.sigma_seed(4, 0), n, with_inverse=True)
+    qd, gd = q.to(dev), g.to(dev)
+    sd, invd, posd = (torch.from_numpy(x).to(dev) for x in (sig, inv, pos))
+    out = torch.empty_like(qd)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, K=200, W=10):
+        for _ in range(W):
+            fn()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(K):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / K
+
+    t_gated = timed(lambda: ssw.gated_sa_swa_decode(qd, kd, vd, sd, invd, posd, w, gd, out=out))
+    t_sa = timed(lambda: ssw.sa_decode(qd, kd, vd, sd, invd, posd, w, out=out))
+    t_swa = timed(lambda: ssw.swa_decode(qd, kd, vd, posd, w, out=out))
+
+    # K/V rows each step must read (per KV head): SA neighbours + SWA window
+    ww = min(w, n)
+    sa_rows = swa_rows = 0
+    for t in pos.tolist():
+        p = int(inv[t])
+        band = sig[max(0, p - ww + 1):min(n, p + ww)]
+        sa_rows += int((band <= t).sum())
+        swa_rows += min(ww, t + 1)
+    row = d * 2
+    kv_bytes = lambda rows: 2 * rows * Hkv * row
+    qo_bytes = 2 * B * Hq * row
+    gated_bytes = kv_bytes(sa_rows + swa_rows) + qo_bytes + 2 * B * Hq * 4
+    sa_bytes = kv_bytes(sa_rows) + qo_bytes
+    swa_bytes = kv_bytes(swa_rows) + qo_bytes
+    gbs = gated_bytes / (t_gated * 1e-3) / 1e9
+    line = {
+        "metric": "gated SA+SWA decode step tokens/s over a KV cache (n_max=32K, w=128, 1 GPU)",
+        "value": round(B / (t_gated * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic: Q,K,V ~ N(0,1), gates sigmoid(N(0,1)), seeded sigma, positions "
+                "uniform in [n_max/2, n_max)",
+        "config": {"workload": "decode, long-context layer shape", "B": B, "n_max": n, "Hq": Hq,
+                   "Hkv": Hkv, "d": d, "window": w},
+        "us_per_step": round(t_gated * 1e3, 2), "sa_us": round(t_sa * 1e3, 2),
+        "swa_us": round(t_swa * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": gated_bytes},
+        "sa_gbs": round(sa_bytes / (t_sa * 1e-3) / 1e9, 1),
+        "swa_gbs": round(swa_bytes / (t_swa * 1e-3) / 1e9, 1),
+        "mean_sa_neighbours": round(sa_rows / B, 1),
+    }
+    log(f"decode B={B}: gated {t_gated * 1e3:.1f} us ({gbs:.0f} GB/s), SA {t_sa * 1e3:.1f} us, "
+        f"SWA {t_swa * 1e3:.1f} us; {sa_rows / B:.1f} SA neighbours per token")
     print(json.dumps(line), flush=True)
 
 

@@ -182,6 +182,39 @@ int ssw_gated_sa_swa_backward(const void* q, const void* k, const void* v, const
                               float* delta, int B, int n, int Hq, int Hkv, int d, int dtype,
                               void* stream);
 
+/* ---- Decode: one new token per batch row over a KV cache ----
+ *
+ * The pages apply SA to pretrained models without training ([SA-ja] 主要な貢献 item 3, 結果),
+ * i.e. generating from a cache, but do not say how sigma evolves as the cache grows.  Reading:
+ * sigma is drawn once per layer over the full context length n_max, and decoding the token at
+ * position t computes exactly row t of causal SA over that length (中核メカニズム, 因果的制約):
+ * the query attends to the cached tokens sigma[q] for slots |q - sigma^-1(t)| <= w - 1 with
+ * sigma[q] <= t, all of which precede t.  The SWA step attends to positions [t - w + 1, t].
+ *   q         device [B, Hq, d]: the new token's query of each batch row.
+ *   k_cache, v_cache  device [B, n_max, Hkv, d]: positions 0..pos[b] of row b filled (the new
+ *             token's own K/V included).  Only positions <= pos[b] are read.
+ *   sigma, inv_sigma  device int32 [n_max]: the layer's permutation and its inverse.
+ *   pos       device int32 [B]: t of each batch row, in [0, n_max) (rows may differ).  A position
+ *             outside that range makes that row's output NaN.
+ *   window    w >= 1 (values >= n_max behave as n_max).
+ *   gate      device float32 [B, Hq] or NULL (single path); gates [2, B, Hq] (gated call).
+ *   out       device [B, Hq, d], overwritten.
+ * Hq / Hkv must be <= 8 (SSW_ESHAPE otherwise).  fp32 or bf16; one kernel launch. */
+int ssw_sa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* sigma,
+                  const int32_t* inv_sigma, const int32_t* pos, int window, const float* gate,
+                  void* out, int B, int n_max, int Hq, int Hkv, int d, int dtype, void* stream);
+
+/* SWA decode step: sigma and inv_sigma must be NULL. */
+int ssw_swa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* sigma,
+                   const int32_t* inv_sigma, const int32_t* pos, int window, const float* gate,
+                   void* out, int B, int n_max, int Hq, int Hkv, int d, int dtype, void* stream);
+
+/* Gated decode step: out = g_sa (.) SA step + g_swa (.) SWA step in one kernel (gates required). */
+int ssw_gated_sa_swa_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* sigma, const int32_t* inv_sigma, const int32_t* pos,
+                            int window, const float* gates, void* out, int B, int n_max, int Hq,
+                            int Hkv, int d, int dtype, void* stream);
+
 /* Host helpers (HOST pointers, no GPU needed). */
 
 /* sigma ~ Uniform(S_n) for one layer ([SA-ja] 中核メカニズム step 1) from a seeded Fisher-Yates

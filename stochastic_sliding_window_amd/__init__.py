@@ -22,6 +22,12 @@ Training (bf16):
     gated_sa_swa_forward_train(q, k, v, sigma, window, causal, gates) -> (out, saved)
     gated_sa_swa_backward(q, k, v, sigma, window, causal, gates, saved, dout) -> (dq, dk, dv, dgates)
 
+Decode (one new token per batch row over a KV cache):
+
+    sa_decode(q, k_cache, v_cache, sigma, inv_sigma, pos, window, gate=None, out=None)
+    swa_decode(q, k_cache, v_cache, pos, window, gate=None, out=None)
+    gated_sa_swa_decode(q, k_cache, v_cache, sigma, inv_sigma, pos, window, gates, out=None)
+
 There is no fallback: if ``libssw.so`` has not been built, importing this package raises.
 """
 
@@ -43,7 +49,8 @@ __all__ = [
     "SSWError", "LIB_PATH", "sa_forward", "swa_forward", "gated_sa_swa_forward",
     "make_permutation", "inverse_permutation", "check_permutation", "neighbor_mask",
     "last_error", "F32", "BF16", "sa_forward_lse", "swa_forward_lse", "sa_backward",
-    "swa_backward", "gated_sa_swa_forward_train", "gated_sa_swa_backward",
+    "swa_backward", "gated_sa_swa_forward_train", "gated_sa_swa_backward", "sa_decode",
+    "swa_decode", "gated_sa_swa_decode",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -72,7 +79,7 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it first with "
-            "`python -m stochastic_sliding_window_amd.build` (needs ROCm hipcc)")
+            "`python stochastic_sliding_window_amd/build.py` (needs ROCm hipcc)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, f32p, i32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
     fwd = [vp, vp, vp, i32p, i32, i32, f32p, vp, i32, i32, i32, i32, i32, i32, vp]
@@ -100,6 +107,11 @@ def _load() -> ctypes.CDLL:
                                               vp, vp, vp, vp, f32p, f32p, i32, i32, i32, i32, i32,
                                               i32, vp]
     lib.ssw_gated_sa_swa_backward.restype = ctypes.c_int
+    dec = [vp, vp, vp, i32p, i32p, i32p, i32, f32p, vp, i32, i32, i32, i32, i32, i32, vp]
+    for name in ("ssw_sa_decode", "ssw_swa_decode", "ssw_gated_sa_swa_decode"):
+        fn = getattr(lib, name)
+        fn.argtypes = dec
+        fn.restype = ctypes.c_int
     lib.ssw_make_permutation.argtypes = [ctypes.c_uint64, i32, i32p, i32p]
     lib.ssw_make_permutation.restype = ctypes.c_int
     lib.ssw_inverse_permutation.argtypes = [i32p, i32, i32p]
@@ -447,3 +459,57 @@ def gated_sa_swa_backward(q, k, v, sigma, window: int, causal: bool, gates, save
         _dev_ptr(dout), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv), _dev_ptr(dgates),
         _dev_ptr(delta), B, n, Hq, k.shape[2], d, _dtype_code(q), _stream_handle(q)))
     return dq, dk, dv, dgates
+
+
+# ------------------------------------------------------------------------------------------
+# decode over a KV cache
+# ------------------------------------------------------------------------------------------
+
+def _decode(fn, q, k_cache, v_cache, sigma, inv_sigma, pos, window, gate, gate_shape, out):
+    torch = _torch()
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous device tensor")
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, Hq, d] and the caches [B, n_max, Hkv, d]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share a dtype")
+    B, Hq, d = q.shape
+    n_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("cache shape does not match q")
+    if sigma is not None:
+        sigma = _prep_sigma(sigma, n_max, q.device)
+        inv_sigma = _prep_sigma(inv_sigma, n_max, q.device)
+    if not isinstance(pos, torch.Tensor) or pos.dtype != torch.int32 or pos.shape != (B,) or \
+            pos.device != q.device or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous int32 [B] tensor on q's device")
+    gate = _prep_gate(gate, gate_shape(B, Hq), q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        out = _prep_like(out, q, "out")
+    _check(fn(_dev_ptr(q), _dev_ptr(k_cache), _dev_ptr(v_cache), _dev_ptr(sigma),
+              _dev_ptr(inv_sigma), _dev_ptr(pos), int(window), _dev_ptr(gate), _dev_ptr(out), B,
+              n_max, Hq, Hkv, d, _dtype_code(q), _stream_handle(q)))
+    return out
+
+
+def sa_decode(q, k_cache, v_cache, sigma, inv_sigma, pos, window: int, gate=None, out=None):
+    """One SA decode step per batch row (ssw_sa_decode): row pos[b] of causal SA over n_max."""
+    return _decode(_lib.ssw_sa_decode, q, k_cache, v_cache, sigma, inv_sigma, pos, window, gate,
+                   lambda B, H: (B, H), out)
+
+
+def swa_decode(q, k_cache, v_cache, pos, window: int, gate=None, out=None):
+    """One SWA decode step per batch row (ssw_swa_decode)."""
+    return _decode(_lib.ssw_swa_decode, q, k_cache, v_cache, None, None, pos, window, gate,
+                   lambda B, H: (B, H), out)
+
+
+def gated_sa_swa_decode(q, k_cache, v_cache, sigma, inv_sigma, pos, window: int, gates, out=None):
+    """g_sa * SA step + g_swa * SWA step, gates [2, B, Hq] (ssw_gated_sa_swa_decode)."""
+    if gates is None:
+        raise ValueError("gates are required")
+    return _decode(_lib.ssw_gated_sa_swa_decode, q, k_cache, v_cache, sigma, inv_sigma, pos,
+                   window, gates, lambda B, H: (2, B, H), out)

@@ -1,6 +1,8 @@
 """Build libssw.so (the C-ABI library with the gfx950 kernels) in-tree with hipcc.
 
-    python -m stochastic_sliding_window_amd.build          # or: python stochastic_sliding_window_amd/build.py
+    python stochastic_sliding_window_amd/build.py
+
+(run as a script: importing the package loads libssw.so, which this script produces)
 
 Produces stochastic_sliding_window_amd/libssw.so.  Every HIP translation unit is compiled with
 packed-fp32 instruction selection turned off (plain fp32 VALU code only).
@@ -26,7 +28,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["ssw_api.cpp", "band_attn.hip", "band_attn_bwd.hip"]
+SOURCES = ["ssw_api.cpp", "band_attn.hip", "band_attn_bwd.hip", "band_decode.hip"]
 
 
 def hipcc() -> str:

@@ -69,6 +69,23 @@ struct BandBwdLaunch {
 
 hipError_t launch_band_attn_bwd(const BandBwdLaunch& a, hipStream_t stream);
 
+// One decode step per batch row over a KV cache (SA and/or SWA, optionally gated).
+struct DecodeLaunch {
+  const void* q;          // [B, Hq, d]
+  const void* k_cache;    // [B, n_max, Hkv, d]
+  const void* v_cache;
+  const int32_t* sigma;   // [n_max] (SA path)
+  const int32_t* inv_sigma;
+  const int32_t* pos;     // [B] device
+  const float* gate;      // paths 1 or 2: [B, Hq] or nullptr; paths 3: [2, B, Hq]
+  void* out;              // [B, Hq, d]
+  int B, n_max, Hq, Hkv, d, dtype;
+  int window;             // already clamped to [1, n_max]
+  int paths;              // bit 0: SA, bit 1: SWA
+};
+
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+
 // out = g_sa * y_sa + g_swa * y_swa for bf16 rows of d elements; gates [2, rows] fp32.
 hipError_t launch_gate_combine(const void* y_sa, const void* y_swa, const float* gates,
                                void* out, int64_t rows, int d, hipStream_t stream);

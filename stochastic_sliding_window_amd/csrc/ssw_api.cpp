@@ -416,6 +416,83 @@ int ssw_gated_sa_swa_backward(const void* q, const void* k, const void* v, const
   return run_bwd(who, a2, s);
 }
 
+// ---- decode: one new token per batch row over a KV cache
+
+static int decode(const char* who, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* sigma, const int32_t* inv_sigma, const int32_t* pos, int window,
+                  const float* gate, void* out, int B, int n_max, int Hq, int Hkv, int d,
+                  int dtype, void* stream, int paths) {
+  const std::string w(who);
+  if (B < 0 || n_max < 1) return fail(SSW_EINVAL, w + ": need B >= 0 and n_max >= 1");
+  if (window < 1) return fail(SSW_EINVAL, w + ": window must be >= 1");
+  if (Hq < 1 || Hkv < 1) return fail(SSW_EINVAL, w + ": Hq and Hkv must be >= 1");
+  if (Hq % Hkv != 0) return fail(SSW_ESHAPE, w + ": Hq must be a multiple of Hkv");
+  if (Hq / Hkv > 8) return fail(SSW_ESHAPE, w + ": at most 8 query heads per KV head");
+  if ((int64_t)B * Hkv >= ((int64_t)1 << 31)) return fail(SSW_ESHAPE, w + ": B * Hkv too large");
+  if (dtype != SSW_F32 && dtype != SSW_BF16) return fail(SSW_EDTYPE, w + ": unsupported dtype");
+  if (d != 64 && d != 128) return fail(SSW_EDTYPE, w + ": head dim d must be 64 or 128");
+  if (B == 0) return SSW_OK;
+  if (!q || !k_cache || !v_cache || !pos || !out)
+    return fail(SSW_EINVAL, w + ": q, k_cache, v_cache, pos and out must be non-NULL");
+  if ((paths & 1) && (!sigma || !inv_sigma))
+    return fail(SSW_EINVAL, w + ": sigma and inv_sigma must be non-NULL");
+  if (paths == 3 && !gate) return fail(SSW_EINVAL, w + ": gates must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(SSW_EALIGN, w + ": q, k_cache, v_cache and out must be 16-byte aligned");
+  if (!aligned(pos, 4) || (sigma && !aligned(sigma, 4)) || (inv_sigma && !aligned(inv_sigma, 4)) ||
+      (gate && !aligned(gate, 4)))
+    return fail(SSW_EALIGN, w + ": pos, sigma, inv_sigma and gate must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if ((paths & 1) && validate_requested()) {
+    int st = check_sigma_on_device(sigma, n_max, s);
+    if (st != SSW_OK) return st;
+  }
+  ssw::DecodeLaunch a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.sigma = sigma;
+  a.inv_sigma = inv_sigma;
+  a.pos = pos;
+  a.gate = gate;
+  a.out = out;
+  a.B = B;
+  a.n_max = n_max;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.dtype = dtype;
+  a.window = window < n_max ? window : n_max;
+  a.paths = paths;
+  hipError_t e = ssw::launch_decode(a, s);
+  if (e != hipSuccess) return fail(SSW_EHIP, w + ": kernel launch failed: " + hipGetErrorString(e));
+  return SSW_OK;
+}
+
+int ssw_sa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* sigma,
+                  const int32_t* inv_sigma, const int32_t* pos, int window, const float* gate,
+                  void* out, int B, int n_max, int Hq, int Hkv, int d, int dtype, void* stream) {
+  return decode("ssw_sa_decode", q, k_cache, v_cache, sigma, inv_sigma, pos, window, gate, out, B,
+                n_max, Hq, Hkv, d, dtype, stream, 1);
+}
+
+int ssw_swa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* sigma,
+                   const int32_t* inv_sigma, const int32_t* pos, int window, const float* gate,
+                   void* out, int B, int n_max, int Hq, int Hkv, int d, int dtype, void* stream) {
+  if (sigma || inv_sigma)
+    return fail(SSW_EINVAL, "ssw_swa_decode: sigma and inv_sigma must be NULL (identity)");
+  return decode("ssw_swa_decode", q, k_cache, v_cache, nullptr, nullptr, pos, window, gate, out,
+                B, n_max, Hq, Hkv, d, dtype, stream, 2);
+}
+
+int ssw_gated_sa_swa_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* sigma, const int32_t* inv_sigma, const int32_t* pos,
+                            int window, const float* gates, void* out, int B, int n_max, int Hq,
+                            int Hkv, int d, int dtype, void* stream) {
+  return decode("ssw_gated_sa_swa_decode", q, k_cache, v_cache, sigma, inv_sigma, pos, window,
+                gates, out, B, n_max, Hq, Hkv, d, dtype, stream, 3);
+}
+
 int ssw_make_permutation(uint64_t seed, int n, int32_t* sigma_out, int32_t* inv_out) {
   if (n < 0) return fail(SSW_EINVAL, "ssw_make_permutation: n must be >= 0");
   if (n > 0 && !sigma_out) return fail(SSW_EINVAL, "ssw_make_permutation: sigma_out is NULL");

@@ -237,3 +237,49 @@ def test_gated_training_checks():
     assert bwd(y_swa=None) == -1
     assert bwd(dgates=P + 1) == -4
     assert bwd(dtype=0) == -3
+
+
+# ---- decode entry points -----------------------------------------------------------------------
+
+for _n in ("ssw_sa_decode", "ssw_swa_decode", "ssw_gated_sa_swa_decode"):
+    getattr(_lib, _n).argtypes = [_VP] * 6 + [_I] + [_VP] * 2 + [_I] * 6 + [_VP]
+    getattr(_lib, _n).restype = _I
+
+DEC_GOOD = dict(q=P, k=P, v=P, sigma=P, inv=P, pos=P, window=8, gate=P, out=P, B=2, n=64, Hq=8,
+                Hkv=2, d=128, dtype=1)
+
+
+def _call_dec(fn, **kw):
+    a = dict(DEC_GOOD)
+    if fn == "ssw_swa_decode":
+        a.update(sigma=None, inv=None)
+    a.update(kw)
+    return getattr(_lib, fn)(a["q"], a["k"], a["v"], a["sigma"], a["inv"], a["pos"], a["window"],
+                             a["gate"], a["out"], a["B"], a["n"], a["Hq"], a["Hkv"], a["d"],
+                             a["dtype"], None)
+
+
+@pytest.mark.parametrize("fn", ["ssw_sa_decode", "ssw_swa_decode", "ssw_gated_sa_swa_decode"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=0), -1),
+    (dict(n=0), -1),
+    (dict(pos=None), -1),
+    (dict(out=None), -1),
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(Hq=32, Hkv=2), -2),      # more than 8 query heads per KV head
+    (dict(d=32), -3),
+    (dict(dtype=5), -3),
+    (dict(q=P + 8), -4),
+    (dict(pos=P + 2), -4),
+])
+def test_decode_bad_arguments_rejected(fn, kw, status):
+    assert _call_dec(fn, **kw) == status
+    assert _lib.ssw_last_error().decode().startswith(fn)
+
+
+def test_decode_specific_checks():
+    assert _call_dec("ssw_sa_decode", sigma=None) == -1
+    assert _call_dec("ssw_sa_decode", inv=None) == -1
+    assert _call_dec("ssw_swa_decode", sigma=P) == -1
+    assert _call_dec("ssw_gated_sa_swa_decode", gate=None) == -1
+    assert _call_dec("ssw_sa_decode", B=0, q=None) == 0
