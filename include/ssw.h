@@ -109,6 +109,25 @@ int ssw_gated_sa_swa_forward_timed(const void* q, const void* k, const void* v,
                                    int d, int dtype, void* stream, void* ev_swa_start,
                                    void* ev_swa_end, void* ev_sa_start, void* ev_sa_end);
 
+/* ---- Variant: one sigma per batch row and/or per KV head ----
+ *
+ * [SA-ja] 中核メカニズム draws one permutation per layer; sharing it across the batch and the
+ * heads is this library's default reading.  These calls let every (batch row b, KV head g) use
+ * its own permutation, found at sigma + b * sigma_batch_stride + g * sigma_head_stride
+ * (elements; each a permutation of [0, n); strides >= 0, and 0 shares it along that axis).  The
+ * query heads of one KV head share its sigma, since they attend to the same gathered K/V rows.
+ * Other arguments as in ssw_sa_forward / ssw_gated_sa_swa_forward (the SWA path of the gated
+ * call needs no sigma).  SSW_VALIDATE=1 checks every permutation used. */
+int ssw_sa_forward_ex(const void* q, const void* k, const void* v, const int32_t* sigma,
+                      int64_t sigma_batch_stride, int64_t sigma_head_stride, int window,
+                      int causal, const float* gate, void* out, int B, int n, int Hq, int Hkv,
+                      int d, int dtype, void* stream);
+
+int ssw_gated_sa_swa_forward_ex(const void* q, const void* k, const void* v, const int32_t* sigma,
+                                int64_t sigma_batch_stride, int64_t sigma_head_stride, int window,
+                                int causal, const float* gates, void* out, int B, int n, int Hq,
+                                int Hkv, int d, int dtype, void* stream);
+
 /* ---- Training: forward with the rows' log-sum-exp, backward, gated forward and backward ----
  *
  * The pages pretrain a model from scratch with the gated layer ([SA-ja] 主要な貢献 item 3 and

@@ -22,6 +22,11 @@ Training (bf16):
     gated_sa_swa_forward_train(q, k, v, sigma, window, causal, gates) -> (out, saved)
     gated_sa_swa_backward(q, k, v, sigma, window, causal, gates, saved, dout) -> (dq, dk, dv, dgates)
 
+Variant: one sigma per batch row and/or KV head (sigma [B, n], [Hkv, n] or [B, Hkv, n]):
+
+    sa_forward_ex(q, k, v, sigmas, window, causal, gate=None, out=None)
+    gated_sa_swa_forward_ex(q, k, v, sigmas, window, causal, gates, out=None)
+
 Decode (one new token per batch row over a KV cache):
 
     sa_decode(q, k_cache, v_cache, sigma, inv_sigma, pos, window, gate=None, out=None)
@@ -50,7 +55,7 @@ __all__ = [
     "make_permutation", "inverse_permutation", "check_permutation", "neighbor_mask",
     "last_error", "F32", "BF16", "sa_forward_lse", "swa_forward_lse", "sa_backward",
     "swa_backward", "gated_sa_swa_forward_train", "gated_sa_swa_backward", "sa_decode",
-    "swa_decode", "gated_sa_swa_decode",
+    "swa_decode", "gated_sa_swa_decode", "sa_forward_ex", "gated_sa_swa_forward_ex",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -111,6 +116,12 @@ def _load() -> ctypes.CDLL:
     for name in ("ssw_sa_decode", "ssw_swa_decode", "ssw_gated_sa_swa_decode"):
         fn = getattr(lib, name)
         fn.argtypes = dec
+        fn.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    for name in ("ssw_sa_forward_ex", "ssw_gated_sa_swa_forward_ex"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, i32p, i64, i64, i32, i32, f32p, vp, i32, i32, i32, i32, i32,
+                       i32, vp]
         fn.restype = ctypes.c_int
     lib.ssw_make_permutation.argtypes = [ctypes.c_uint64, i32, i32p, i32p]
     lib.ssw_make_permutation.restype = ctypes.c_int
@@ -513,3 +524,53 @@ def gated_sa_swa_decode(q, k_cache, v_cache, sigma, inv_sigma, pos, window: int,
         raise ValueError("gates are required")
     return _decode(_lib.ssw_gated_sa_swa_decode, q, k_cache, v_cache, sigma, inv_sigma, pos,
                    window, gates, lambda B, H: (2, B, H), out)
+
+
+# ------------------------------------------------------------------------------------------
+# variant: one sigma per batch row and/or KV head
+# ------------------------------------------------------------------------------------------
+
+def _sigma_strides(sigmas, B, n, Hkv, device):
+    """(batch stride, head stride) of a sigma tensor [n], [B, n], [Hkv, n] or [B, Hkv, n]."""
+    torch = _torch()
+    if not isinstance(sigmas, torch.Tensor) or sigmas.dtype != torch.int32 or \
+            not sigmas.is_contiguous() or sigmas.device != device or sigmas.shape[-1] != n:
+        raise ValueError("sigmas must be a contiguous int32 tensor [..., n] on q's device")
+    shape = tuple(sigmas.shape[:-1])
+    if shape == ():
+        return 0, 0
+    if shape == (B, Hkv):
+        return Hkv * n, n
+    if shape == (B,) and B != Hkv:
+        return n, 0
+    if shape == (Hkv,) and B != Hkv:
+        return 0, n
+    raise ValueError(f"sigmas must be [n], [B, n], [Hkv, n] or [B, Hkv, n] (B = Hkv needs the "
+                     f"3-D form); got {tuple(sigmas.shape)}")
+
+
+def sa_forward_ex(q, k, v, sigmas, window: int, causal: bool, gate=None, out=None):
+    """SA forward with one sigma per batch row and/or KV head (ssw_sa_forward_ex)."""
+    out = _prep(q, k, v, out)
+    B, n, Hq, d = q.shape
+    sb, sh = _sigma_strides(sigmas, B, n, k.shape[2], q.device)
+    gate = _prep_gate(gate, (B, n, Hq), q.device)
+    _check(_lib.ssw_sa_forward_ex(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sigmas), sb, sh,
+                                  int(window), int(bool(causal)), _dev_ptr(gate), _dev_ptr(out),
+                                  B, n, Hq, k.shape[2], d, _dtype_code(q), _stream_handle(q)))
+    return out
+
+
+def gated_sa_swa_forward_ex(q, k, v, sigmas, window: int, causal: bool, gates, out=None):
+    """Gated SA+SWA forward with one sigma per batch row and/or KV head."""
+    out = _prep(q, k, v, out)
+    B, n, Hq, d = q.shape
+    sb, sh = _sigma_strides(sigmas, B, n, k.shape[2], q.device)
+    if gates is None:
+        raise ValueError("gates are required")
+    gates = _prep_gate(gates, (2, B, n, Hq), q.device)
+    _check(_lib.ssw_gated_sa_swa_forward_ex(_dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sigmas),
+                                            sb, sh, int(window), int(bool(causal)), _dev_ptr(gates),
+                                            _dev_ptr(out), B, n, Hq, k.shape[2], d, _dtype_code(q),
+                                            _stream_handle(q)))
+    return out

@@ -23,6 +23,9 @@ struct BandLaunch {
   const void* k;
   const void* v;
   const int32_t* sigma;  // device int32[n] when perm, else ignored
+  // sigma of (batch row b, KV head g) starts at sigma + b * sig_bstride + g * sig_hstride
+  int64_t sig_bstride = 0;
+  int64_t sig_hstride = 0;
   const float* gate;     // device float32 [B, n, Hq] or nullptr
   void* out;
   int B, n, Hq, Hkv, d;

@@ -224,6 +224,8 @@ struct Params {
   const char* k;
   const char* v;
   const int32_t* sigma;
+  int64_t sig_bstride;  // sigma of (batch row b, KV head g) at sigma + b * sig_bstride +
+  int64_t sig_hstride;  // g * sig_hstride (both 0: one sigma shared by every row and head)
   const float* gate;
   char* out;
   float* lse;        // natural-log log-sum-exp of each row [B, n, Hq], or nullptr
@@ -297,7 +299,8 @@ void band_attn_kernel(Params prm) {
   const uint32_t kv_range = (uint32_t)((int64_t)(n - 1) * kv_row_stride + Lay::kRowBytes);
   const i32x4 rs_k = make_rsrc(prm.k + kv_base, kv_range);
   const i32x4 rs_v = make_rsrc(prm.v + kv_base, kv_range);
-  const i32x4 rs_sig = make_rsrc(prm.sigma, PERM ? (uint32_t)n * 4u : 0u);
+  const int32_t* sigma = prm.sigma + (b * prm.sig_bstride + g * prm.sig_hstride);
+  const i32x4 rs_sig = make_rsrc(sigma, PERM ? (uint32_t)n * 4u : 0u);
 
   // sigma of keys [seg_key0, seg_key0 + 32 * nseg_chunks) into LDS (permuted operator only)
   auto dma_sigma = [&](int seg_key0, int nseg_chunks) {
@@ -404,7 +407,7 @@ void band_attn_kernel(Params prm) {
   int myorig = myslot;
   if constexpr (PERM) {
     dma_sigma(kbeg, min(nchunks, kSegChunks));
-    myorig = prm.sigma[myslot];
+    myorig = sigma[myslot];
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -1171,6 +1174,8 @@ hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream) {
   prm.k = (const char*)a.k;
   prm.v = (const char*)a.v;
   prm.sigma = a.sigma;
+  prm.sig_bstride = a.sig_bstride;
+  prm.sig_hstride = a.sig_hstride;
   prm.gate = a.gate;
   prm.out = (char*)a.out;
   prm.lse = a.lse;

@@ -212,6 +212,71 @@ int ssw_gated_sa_swa_forward_timed(const void* q, const void* k, const void* v,
                n, Hq, Hkv, d, dtype, stream, events);
 }
 
+// ---- one sigma per batch row and/or per KV head
+
+static int check_sigma_set(const int32_t* sigma, int64_t sb, int64_t sh, int B, int n, int Hkv,
+                           hipStream_t s) {
+  for (int b = 0; b < (sb ? B : 1); ++b)
+    for (int g = 0; g < (sh ? Hkv : 1); ++g) {
+      const int st = check_sigma_on_device(sigma + b * sb + g * sh, n, s);
+      if (st != SSW_OK) return st;
+    }
+  return SSW_OK;
+}
+
+static int forward_ex(const char* who, const void* q, const void* k, const void* v,
+                      const int32_t* sigma, int64_t sb, int64_t sh, int window, int causal,
+                      const float* gates, void* out, int B, int n, int Hq, int Hkv, int d,
+                      int dtype, void* stream, bool gated_call) {
+  int st = check_forward(who, q, k, v, out, window, causal, B, n, Hq, Hkv, d, dtype);
+  if (st != SSW_OK || B == 0 || n == 0) return st;
+  if (!sigma) return fail(SSW_EINVAL, std::string(who) + ": sigma must be non-NULL");
+  if (gated_call && !gates) return fail(SSW_EINVAL, std::string(who) + ": gates must be non-NULL");
+  if (sb < 0 || sh < 0)
+    return fail(SSW_EINVAL, std::string(who) + ": sigma strides must be >= 0");
+  if (!aligned(sigma, 4) || (gates && !aligned(gates, 4)))
+    return fail(SSW_EALIGN, std::string(who) + ": sigma and gates must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (validate_requested()) {
+    st = check_sigma_set(sigma, sb, sh, B, n, Hkv, s);
+    if (st != SSW_OK) return st;
+  }
+  if (!gated_call) {
+    ssw::BandLaunch a =
+        make_launch(q, k, v, sigma, window, causal, gates, out, B, n, Hq, Hkv, d, dtype);
+    a.sig_bstride = sb;
+    a.sig_hstride = sh;
+    return run(who, a, s);
+  }
+  ssw::BandLaunch a1 = make_launch(q, k, v, nullptr, window, causal, gates + (size_t)B * n * Hq,
+                                   out, B, n, Hq, Hkv, d, dtype);
+  a1.epilogue = ssw::kEpiPartial;
+  ssw::BandLaunch a2 =
+      make_launch(q, k, v, sigma, window, causal, gates, out, B, n, Hq, Hkv, d, dtype);
+  a2.epilogue = ssw::kEpiAddPartial;
+  a2.sig_bstride = sb;
+  a2.sig_hstride = sh;
+  if ((st = run(who, a1, s)) != SSW_OK) return st;
+  return run(who, a2, s);
+}
+
+int ssw_sa_forward_ex(const void* q, const void* k, const void* v, const int32_t* sigma,
+                      int64_t sigma_batch_stride, int64_t sigma_head_stride, int window,
+                      int causal, const float* gate, void* out, int B, int n, int Hq, int Hkv,
+                      int d, int dtype, void* stream) {
+  return forward_ex("ssw_sa_forward_ex", q, k, v, sigma, sigma_batch_stride, sigma_head_stride,
+                    window, causal, gate, out, B, n, Hq, Hkv, d, dtype, stream, false);
+}
+
+int ssw_gated_sa_swa_forward_ex(const void* q, const void* k, const void* v, const int32_t* sigma,
+                                int64_t sigma_batch_stride, int64_t sigma_head_stride, int window,
+                                int causal, const float* gates, void* out, int B, int n, int Hq,
+                                int Hkv, int d, int dtype, void* stream) {
+  return forward_ex("ssw_gated_sa_swa_forward_ex", q, k, v, sigma, sigma_batch_stride,
+                    sigma_head_stride, window, causal, gates, out, B, n, Hq, Hkv, d, dtype, stream,
+                    true);
+}
+
 // ---- training: forward with the rows' log-sum-exp, backward, gated forward/backward
 
 static int forward_lse(const char* who, const void* q, const void* k, const void* v,

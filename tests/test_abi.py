@@ -283,3 +283,18 @@ def test_decode_specific_checks():
     assert _call_dec("ssw_swa_decode", sigma=P) == -1
     assert _call_dec("ssw_gated_sa_swa_decode", gate=None) == -1
     assert _call_dec("ssw_sa_decode", B=0, q=None) == 0
+
+
+def test_strided_sigma_checks():
+    for fn in ("ssw_sa_forward_ex", "ssw_gated_sa_swa_forward_ex"):
+        f = getattr(_lib, fn)
+        f.argtypes = [_VP] * 4 + [ctypes.c_int64] * 2 + [_I] * 2 + [_VP] * 2 + [_I] * 6 + [_VP]
+        f.restype = _I
+        args = lambda sig=P, sb=0, sh=0, gate=P: (P, P, P, sig, sb, sh, 8, 1, gate, P, 1, 64, 4, 2,
+                                                  64, 1, None)
+        assert f(*args(sig=None)) == -1
+        assert f(*args(sb=-1)) == -1
+        assert f(*args(sh=-64)) == -1
+        assert f(*args(sig=P + 2)) == -4
+    assert _lib.ssw_gated_sa_swa_forward_ex(P, P, P, P, 0, 0, 8, 1, None, P, 1, 64, 4, 2, 64, 1,
+                                            None) == -1
