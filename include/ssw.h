@@ -256,6 +256,19 @@ int ssw_check_permutation(const int32_t* sigma, int n);
 int ssw_neighbor_mask(const int32_t* sigma, int n, int window, int causal, uint32_t* bits,
                       void* stream);
 
+/* Receptive-field growth over depth, for the theory check of [SA-ja] 理論的性質 (受容野の
+ * 成長): SWA's field grows linearly with depth, SA's exponentially, and full coverage takes
+ * O(log_w n) SA layers.  Host computation, no GPU.
+ *   With the neighbour sets of the attention kernels (mode 0: SA, 1: SWA, 2: the gated layer's
+ *   union of both; causal 0 or 1) and layer l's sigma = ssw_make_permutation(seeds[l], n):
+ *     R_0(i) = {i},   R_l(i) = union of R_{l-1}(j) over the neighbours j of i at layer l.
+ *   coverage_out[l - 1] = sum_i |R_l(i)| / (number of pairs): the share of pairs (j <= i when
+ *   causal, all n^2 otherwise) whose information has reached i after l layers.
+ *   n in [1, 32768] (memory ~ n^2 / 4 bytes); seeds (host, `layers` entries; NULL allowed for
+ *   mode 1); coverage_out (host, `layers` doubles). */
+int ssw_receptive_field_coverage(int n, int window, int layers, const uint64_t* seeds, int mode,
+                                 int causal, double* coverage_out);
+
 /* Message describing the most recent failed call on the calling thread ("" if none). */
 const char* ssw_last_error(void);
 

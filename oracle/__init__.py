@@ -16,6 +16,7 @@ definitions on the pages:
 * backward.py    -- the gradients of those forwards (chain rule through the definition, one
   query row at a time), the rows' log-sum-exp, and sampled-row forms for large n.
 * decode.py      -- one decode step over a KV cache (row t of causal SA over the full context).
+* coverage.py    -- receptive-field growth over layers (sets, small n).
 
 Sources (the pages):
   [SA-ja] "技術的概要：確率的アテンション" (gist.science/ja/paper/2604.00754) -- Stochastic
@@ -51,6 +52,7 @@ from .backward import (
     attending_queries,
 )
 from .decode import sa_decode, swa_decode, gated_decode
+from .coverage import coverage_by_layer
 
 __all__ = [
     "splitmix64_stream",
@@ -74,4 +76,5 @@ __all__ = [
     "sa_decode",
     "swa_decode",
     "gated_decode",
+    "coverage_by_layer",
 ]

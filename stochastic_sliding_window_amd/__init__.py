@@ -56,6 +56,7 @@ __all__ = [
     "last_error", "F32", "BF16", "sa_forward_lse", "swa_forward_lse", "sa_backward",
     "swa_backward", "gated_sa_swa_forward_train", "gated_sa_swa_backward", "sa_decode",
     "swa_decode", "gated_sa_swa_decode", "sa_forward_ex", "gated_sa_swa_forward_ex",
+    "receptive_field_coverage",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -123,6 +124,8 @@ def _load() -> ctypes.CDLL:
         fn.argtypes = [vp, vp, vp, i32p, i64, i64, i32, i32, f32p, vp, i32, i32, i32, i32, i32,
                        i32, vp]
         fn.restype = ctypes.c_int
+    lib.ssw_receptive_field_coverage.argtypes = [i32, i32, i32, vp, i32, i32, vp]
+    lib.ssw_receptive_field_coverage.restype = ctypes.c_int
     lib.ssw_make_permutation.argtypes = [ctypes.c_uint64, i32, i32p, i32p]
     lib.ssw_make_permutation.restype = ctypes.c_int
     lib.ssw_inverse_permutation.argtypes = [i32p, i32, i32p]
@@ -170,6 +173,18 @@ def inverse_permutation(sigma) -> np.ndarray:
     inv = np.empty_like(s)
     _check(_lib.ssw_inverse_permutation(_np_ptr(s), s.shape[0], _np_ptr(inv)))
     return inv
+
+
+def receptive_field_coverage(n: int, window: int, seeds, mode: str = "sa",
+                             causal: bool = True) -> np.ndarray:
+    """Coverage after each layer (ssw_receptive_field_coverage); one seed per layer, mode 'sa',
+    'swa' or 'gated'."""
+    modes = {"sa": 0, "swa": 1, "gated": 2}
+    sd = np.ascontiguousarray(np.asarray([int(x) & (2**64 - 1) for x in seeds], dtype=np.uint64))
+    out = np.empty(sd.shape[0], dtype=np.float64)
+    _check(_lib.ssw_receptive_field_coverage(int(n), int(window), sd.shape[0], _np_ptr(sd),
+                                             modes[mode], int(bool(causal)), _np_ptr(out)))
+    return out
 
 
 def check_permutation(sigma) -> bool:

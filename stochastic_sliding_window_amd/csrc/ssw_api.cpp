@@ -9,6 +9,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -611,6 +612,55 @@ int ssw_neighbor_mask(const int32_t* sigma, int n, int window, int causal, uint3
   hipError_t e = ssw::launch_neighbor_mask(sigma, n, w, causal != 0, bits, (hipStream_t)stream);
   if (e != hipSuccess)
     return fail(SSW_EHIP, std::string("ssw_neighbor_mask: launch failed: ") + hipGetErrorString(e));
+  return SSW_OK;
+}
+
+// Receptive-field growth of SA / SWA / gated layers ([SA-ja] 理論的性質, 受容野の成長).
+// R_0(i) = {i}; R_l(i) = union of R_{l-1}(j) over the neighbours j of i at layer l (the
+// attention kernels' neighbour sets); coverage = sum |R_l(i)| / (number of pairs j <= i when
+// causal, n^2 otherwise).  Bit rows of n bits, double-buffered; in causal mode row i only has
+// bits <= i, so only its first i / 64 + 1 words are touched.
+int ssw_receptive_field_coverage(int n, int window, int layers, const uint64_t* seeds, int mode,
+                                 int causal, double* coverage_out) {
+  if (n < 1 || n > 32768 || window < 1 || layers < 0 || mode < 0 || mode > 2 ||
+      (causal != 0 && causal != 1))
+    return fail(SSW_EINVAL, "ssw_receptive_field_coverage: need 1 <= n <= 32768, window >= 1, "
+                            "layers >= 0, mode 0 (SA), 1 (SWA) or 2 (gated), causal 0 or 1");
+  if (layers > 0 && (!coverage_out || (mode != 1 && !seeds)))
+    return fail(SSW_EINVAL, "ssw_receptive_field_coverage: seeds and coverage_out are required");
+  const size_t words = ((size_t)n + 63) / 64;
+  std::vector<uint64_t> cur((size_t)n * words, 0), nxt((size_t)n * words, 0);
+  for (int i = 0; i < n; ++i) cur[(size_t)i * words + i / 64] = 1ull << (i % 64);
+  std::vector<int32_t> sigma((size_t)n), inv((size_t)n);
+  const int w = window < n ? window : n;
+  const double total = causal ? (double)n * (n + 1) / 2.0 : (double)n * n;
+  for (int l = 0; l < layers; ++l) {
+    if (mode != 1) ssw_make_permutation(seeds[l], n, sigma.data(), inv.data());
+    std::fill(nxt.begin(), nxt.end(), 0ull);
+    for (int i = 0; i < n; ++i) {
+      uint64_t* dst = &nxt[(size_t)i * words];
+      const size_t used = causal ? (size_t)i / 64 + 1 : words;
+      auto merge = [&](int j) {
+        const uint64_t* src = &cur[(size_t)j * words];
+        for (size_t k = 0; k < used; ++k) dst[k] |= src[k];
+      };
+      if (mode != 1) {  // SA: slots within w - 1 of sigma^-1(i) (holding tokens <= i if causal)
+        const int p = inv[(size_t)i];
+        const int lo = p - (w - 1) > 0 ? p - (w - 1) : 0;
+        const int hi = p + (w - 1) < n - 1 ? p + (w - 1) : n - 1;
+        for (int q = lo; q <= hi; ++q)
+          if (!causal || sigma[(size_t)q] <= i) merge(sigma[(size_t)q]);
+      }
+      if (mode != 0) {  // SWA: [i - w + 1, i], or |i - j| <= w - 1
+        const int hi = causal ? i : (i + (w - 1) < n - 1 ? i + (w - 1) : n - 1);
+        for (int j = i - (w - 1) > 0 ? i - (w - 1) : 0; j <= hi; ++j) merge(j);
+      }
+    }
+    cur.swap(nxt);
+    uint64_t bits = 0;
+    for (uint64_t x : cur) bits += (uint64_t)__builtin_popcountll(x);
+    coverage_out[l] = (double)bits / total;
+  }
   return SSW_OK;
 }
 
