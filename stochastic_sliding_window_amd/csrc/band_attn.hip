@@ -67,6 +67,17 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 #ifndef SSW_PIPELINE
 #define SSW_PIPELINE 1  // scores of chunk c + 1 computed alongside the softmax of chunk c
 #endif
+// The identity-sigma (SWA) kernels hold no sigma in LDS and fewer registers without the score
+// pipeline, so they fit three waves per SIMD (three workgroups per CU) with a three-stage ring.
+#ifndef SSW_WPE_SWA
+#define SSW_WPE_SWA 3
+#endif
+#ifndef SSW_STAGES_SWA
+#define SSW_STAGES_SWA 3
+#endif
+#ifndef SSW_PIPELINE_SWA
+#define SSW_PIPELINE_SWA 0
+#endif
 #ifndef SSW_XCD_REMAP
 #define SSW_XCD_REMAP 1
 #endif
@@ -175,7 +186,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PERM>
 struct Layout {
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int kRowBytes = D * (int)sizeof(T);
@@ -185,13 +196,16 @@ struct Layout {
   static constexpr int kDmaK = kMatBytes / 1024;        // DMA instructions per chunk and matrix
   static constexpr int kDmaPerWave = 2 * kDmaK / kWaves;
   static constexpr int kStageBytes = 2 * kMatBytes;
+  // sigma of a segment of keys (permuted operator only)
+  static constexpr int kSigBytes = PERM ? kSigCap * 4 : 0;
   // ring depth: the configured number of stages, or fewer if they would not fit in 160 KB of LDS
-  static constexpr int kNS = kStages * kStageBytes + kSigCap * 4 <= 163840
-                                 ? kStages
-                                 : (163840 - kSigCap * 4) / kStageBytes;
+  static constexpr int kWant = PERM ? kStages : SSW_STAGES_SWA;
+  static constexpr int kNS = kWant * kStageBytes + kSigBytes <= 163840
+                                 ? kWant
+                                 : (163840 - kSigBytes) / kStageBytes;
   static constexpr int kPF = kNS - 1;  // chunks in flight
   static constexpr int kSigOff = kNS * kStageBytes;
-  static constexpr int kSmem = kSigOff + kSigCap * 4;
+  static constexpr int kSmem = kSigOff + (PERM ? kSigBytes : 16);
   static_assert(kGran >= 8, "V swizzle needs 8 granules per row");
   static_assert(kNS >= 3, "the software pipeline needs at least three stages");
   static_assert((2 * kDmaK) % kWaves == 0 && kDmaK % kDmaPerWave == 0, "DMA split");
@@ -248,10 +262,15 @@ __device__ __forceinline__ int xcd_local_order(int i, int nblocks) {
   return i;
 }
 
+template <typename T, bool PERM>
+constexpr int kWavesPerEU = (PERM || sizeof(T) != 2) ? SSW_WPE : SSW_WPE_SWA;
+
 template <typename T, int D, bool PERM, bool SIGMASK, int EPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SSW_WPE, SSW_WPE)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kWavesPerEU<T, PERM>, kWavesPerEU<T, PERM>)))
 void band_attn_kernel(Params prm) {
-  using Lay = Layout<T, D>;
+  using Lay = Layout<T, D, PERM>;
+  constexpr bool kPipe = PERM ? SSW_PIPELINE : SSW_PIPELINE_SWA;
   constexpr bool kBf16 = Lay::kBf16;
   __shared__ __attribute__((aligned(16))) char smem[Lay::kSmem];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;  // LDS byte address of smem
@@ -365,7 +384,7 @@ void band_attn_kernel(Params prm) {
   // wave's columns i * (1024 / RB) ..., lane l granule l % kGran of column i * (1024 / RB) +
   // l / kGran; granules are XOR-swizzled by column so the epilogue's reads spread over banks.
   // bf16 with a 4-slot ring: two chunks per loop step; the prologue then fetches one step
-  constexpr bool kStep2 = SSW_STEP2 && SSW_PIPELINE && kBf16 && Lay::kNS == 4;
+  constexpr bool kStep2 = SSW_STEP2 && kPipe && kBf16 && Lay::kNS == 4;
   constexpr int kPro = kStep2 ? 2 : Lay::kPF;
   // (needs kWaves / 2 ring stages besides the last chunk's)
   constexpr bool kPrefetchPartial =
@@ -904,7 +923,6 @@ void band_attn_kernel(Params prm) {
       });
     }
 
-#if SSW_STEP2 && SSW_PIPELINE
     if constexpr (kStep2) {
       // Steps of two chunks: step i uses ring slots 2i % 4 and 2i % 4 + 1; after its barrier
       // (step i - 1 consumed) the next step's two chunks are fetched into step i - 1's slots.
@@ -939,9 +957,7 @@ void band_attn_kernel(Params prm) {
           }
         });
       }
-    } else {
-#endif
-#if SSW_PIPELINE
+    } else if constexpr (kPipe) {
     // Software pipeline: while chunk cs is consumed (softmax + P*V from its V), the scores of
     // chunk cs + 1 are already computed from its K, so each wave has independent MFMA work to
     // overlap with the softmax VALU work.  Chunk cs + kPF is fetched meanwhile.
@@ -1001,11 +1017,7 @@ void band_attn_kernel(Params prm) {
         }
       });
     }
-#if SSW_STEP2 && SSW_PIPELINE
-    }
-#endif
-  }
-#else
+    } else {
     // Chunk cs is consumed in iteration cs (scores, softmax, P*V) while chunks cs + 1 .. cs + kPF
     // are in flight; the fetch of chunk cs + kPF reuses the slot of chunk cs - 1.
     auto active = [&](int c) { return wave_on && c >= c_first && c <= c_last; };
@@ -1045,8 +1057,8 @@ void band_attn_kernel(Params prm) {
         }
       });
     }
+    }
   }
-#endif
 
   // ---- epilogue: normalise, gate, scatter to original row sigma[p]
   const float l_tot = pair_sum(l_run);

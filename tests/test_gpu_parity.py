@@ -301,14 +301,14 @@ def test_identity_sigma_matches_swa_kernel():
     _, dev = _data(77, B, n, Hq, Hkv, d, "bf16")
     q, k, v, _ = dev
     ident = torch.arange(n, dtype=torch.int32, device=DEV)
-    # non-causal: the two specialisations do the same arithmetic in the same order
-    a = ssw.sa_forward(q, k, v, ident, w, False)
-    b = ssw.swa_forward(q, k, v, w, False)
-    assert torch.equal(a, b)
-    # causal: same neighbour sets, different key traversal -> equal up to rounding
-    a = ssw.sa_forward(q, k, v, ident, w, True)
-    b = ssw.swa_forward(q, k, v, w, True)
-    assert (a.float() - b.float()).abs().max().item() <= 1e-2
+    # Same neighbour sets in both modes.  The two specialisations differ in loop structure (the
+    # permuted one consumes two 32-key chunks per step and keeps a lazy running maximum per 64
+    # keys; the identity one, sized for three waves per SIMD, one chunk per step; causal SWA also
+    # skips the keys right of the query), so they agree up to bf16 rounding, not bit for bit.
+    for causal in (False, True):
+        a = ssw.sa_forward(q, k, v, ident, w, causal)
+        b = ssw.swa_forward(q, k, v, w, causal)
+        assert (a.float() - b.float()).abs().max().item() <= 1e-2
 
 
 # --------------------------------------------------------------------------------------------
