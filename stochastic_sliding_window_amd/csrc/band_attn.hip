@@ -78,6 +78,9 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 #ifndef SSW_PIPELINE_SWA
 #define SSW_PIPELINE_SWA 0
 #endif
+#ifndef SSW_PREFETCH_PARTIAL
+#define SSW_PREFETCH_PARTIAL 1  // gated SA pass: intermediate rows fetched during the last chunk
+#endif
 #ifndef SSW_XCD_REMAP
 #define SSW_XCD_REMAP 1
 #endif
@@ -388,7 +391,7 @@ void band_attn_kernel(Params prm) {
   constexpr int kPro = kStep2 ? 2 : Lay::kPF;
   // (needs kWaves / 2 ring stages besides the last chunk's)
   constexpr bool kPrefetchPartial =
-      EPI == kEpiAddPartial && kBf16 && Lay::kNS - 1 >= (kWaves + 1) / 2;
+      SSW_PREFETCH_PARTIAL && EPI == kEpiAddPartial && kBf16 && Lay::kNS - 1 >= (kWaves + 1) / 2;
   const int64_t out_batch_bytes = (int64_t)n * prm.Hq * D * (int)sizeof(T);
   const i32x4 rs_out =
       make_rsrc(prm.out + (int64_t)b * out_batch_bytes, (uint32_t)out_batch_bytes);
@@ -679,45 +682,38 @@ void band_attn_kernel(Params prm) {
       const char* Kst = smem + STAGE * Lay::kStageBytes;
       const char* Kn = smem + (NEXT >= 0 ? NEXT : 0) * Lay::kStageBytes;
 
-      // mask.  Register r holds key kc0 + 16(r/8) + 8*h32 + r%8.
-      int sk[16];
+      // mask.  Register r holds key kc0 + 16(r/8) + 8*h32 + r%8.  The causal test folds into a
+      // 16-bit mask as sigma is read, so no sigma value stays live in a register.
+      uint32_t cm = 0xFFFFu;
       if constexpr (SIGMASK) {
         const int* sp = sig_lds + (kc0 - seg_key0);
+        cm = 0u;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const u32x4 a = *(const u32x4*)(sp + 16 * half + 8 * h32);
           const u32x4 bq = *(const u32x4*)(sp + 16 * half + 8 * h32 + 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            sk[8 * half + e] = (int)a[e];
-            sk[8 * half + 4 + e] = (int)bq[e];
+            cm |= (uint32_t)((int)a[e] <= myorig) << (8 * half + e);
+            cm |= (uint32_t)((int)bq[e] <= myorig) << (8 * half + 4 + e);
           }
         }
       }
       float sm[16];
       if (interior) {
-        // all compares first (each into its own lane mask), then the selects: no compare is
-        // followed directly by the select that reads its mask
-        bool ok[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          ok[r] = true;
-          if constexpr (SIGMASK) ok[r] = sk[r] <= myorig;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm[r] = ok[r] ? s[r] : -INFINITY;
+        for (int r = 0; r < 16; ++r) sm[r] = ((cm >> r) & 1u) ? s[r] : -INFINITY;
       } else {
         const int a = max(max(myslot - L, 0) - kc0, 0);
         const int z = min(min(myslot + R, n - 1) - kc0, 31);
         const uint32_t upto = z < 0 ? 0u : (0xFFFFFFFFu >> (31 - z));
         const uint32_t from = a > 31 ? 0u : (0xFFFFFFFFu << a);
         const uint32_t bm = (upto & from) >> (8 * h32);
+        // band bit of register r is bit 16(r/8) + r%8 of bm; keep both tests in one mask
+        const uint32_t band16 = (bm & 0xFFu) | ((bm >> 8) & 0xFF00u);
+        const uint32_t all = band16 & cm;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          bool ok = (bm >> (16 * (r >> 3) + (r & 7))) & 1u;
-          if constexpr (SIGMASK) ok = ok & (sk[r] <= myorig);
-          sm[r] = ok ? s[r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) sm[r] = ((all >> r) & 1u) ? s[r] : -INFINITY;
       }
 
       // scores of the next chunk, interleaved with the column max and the first weights
@@ -1099,9 +1095,14 @@ void band_attn_kernel(Params prm) {
           *dst = u32x2{w[0], w[1]};
         } else {
           if constexpr (EPI == kEpiAddPartial) {
-            // granule d0 / 8 of the row, swizzled by column; bytes 8 * h32 within it
-            const int gsw = ((d0 >> 3) ^ ((lane & 31) & (Lay::kGran - 1)));
-            const u32x2 old = *(const u32x2*)(prow + 16 * gsw + 8 * h32);
+            u32x2 old;
+            if constexpr (kPrefetchPartial) {
+              // granule d0 / 8 of the row, swizzled by column; bytes 8 * h32 within it
+              const int gsw = ((d0 >> 3) ^ ((lane & 31) & (Lay::kGran - 1)));
+              old = *(const u32x2*)(prow + 16 * gsw + 8 * h32);
+            } else {
+              old = *dst;  // not prefetched: read the intermediate where it lies
+            }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
               y[2 * u] += (float)__builtin_bit_cast(_Float16, (uint16_t)(old[u] & 0xffffu)) *
