@@ -32,6 +32,7 @@
 #include <stdint.h>
 
 #include "band_attn.h"
+#include "lds_dma.h"
 
 namespace ssw {
 namespace bwd {
@@ -180,15 +181,23 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const char* p) {
 // ------------------------------------------------------------------------------------------------
 // dQ (and Delta, dg): query-major
 // ------------------------------------------------------------------------------------------------
+constexpr int kDqStages = 4;  // LDS ring of K/V chunks: three in flight while one is consumed
+
 template <int D, bool PERM, bool SIGMASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(Params prm) {
   using LY = Lay<D>;
-  constexpr int kStage = 2 * LY::kMat + kChunk * 4;  // K, V, sigma of the chunk's keys
-  constexpr int kSigOff = 2 * kStage;
+  constexpr int kStage = 2 * LY::kMat;                // K rows, then V rows, of one chunk
+  constexpr int kPF = kDqStages - 1;                  // chunks in flight
+  constexpr int kSigOff = kDqStages * kStage;
   constexpr int kSegChunks = kSigCap / kChunk;        // chunks whose keys' sigma fit in LDS
+  constexpr int kRowsPerDma = 1024 / LY::kRowBytes;   // rows one 64-lane 16-byte DMA covers
+  constexpr int kDmaMat = LY::kMat / 1024;            // DMA instructions per matrix and chunk
+  constexpr int kDW = 2 * kDmaMat / 4;                // per wave (4 waves)
+  static_assert(kDW >= 1 && 2 * kDmaMat == 4 * kDW, "DMA split");
   __shared__ __attribute__((aligned(16))) char smem[kSigOff + (PERM ? kSigCap * 4 : 0)];
   int* sig_lds = (int*)(smem + kSigOff);
+  const uint32_t smem_lds = lds_dma::lds_addr(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -227,8 +236,56 @@ void bwd_dq_kernel(Params prm) {
   const int c_first = (max(0, w_slo - L) - kbeg) / kChunk;
   const int c_last = (min(n - 1, w_shi + R) - kbeg) / kChunk;
 
-  // ---- prologue: Q and dy rows as B operands (k step kb holds d = 16kb + 8h32 + [0, 8)),
-  // Delta and dg from dy and A
+  // ---- K/V rows of this (batch row, KV head): buffer resources, rows addressed by token
+  const uint32_t row_stride = (uint32_t)(prm.Hkv * LY::kRowBytes);
+  const int64_t kv_base = ((int64_t)b * n * prm.Hkv + g) * LY::kRowBytes;
+  const uint32_t kv_range = (uint32_t)((int64_t)(n - 1) * row_stride + LY::kRowBytes);
+  const lds_dma::i32x4 rs_k = lds_dma::resource(prm.k + kv_base, kv_range);
+  const lds_dma::i32x4 rs_v = lds_dma::resource(prm.v + kv_base, kv_range);
+  // this wave's DMA instructions of a chunk: instruction I (wave * kDW + i) brings rows
+  // kRowsPerDma * (I % kDmaMat) + lane / kGran of matrix I / kDmaMat; lane l writes LDS slot
+  // l % kGran of its row, which holds granule (l % kGran) ^ (row % kGran) of that row
+  int dma_row[kDW];
+  uint32_t dma_goff[kDW];
+#pragma unroll
+  for (int i = 0; i < kDW; ++i) {
+    const int I = wave * kDW + i;
+    const int row = kRowsPerDma * (I % kDmaMat) + lane / LY::kGran;
+    dma_row[i] = row;
+    dma_goff[i] = (uint32_t)((((lane % LY::kGran) ^ (row & (LY::kGran - 1)))) << 4);
+  }
+  int seg_key0 = kbeg;  // first key of the current sigma segment
+  auto orig_of_key = [&](int key) { return PERM ? sig_lds[key - seg_key0] : key; };
+  // keys past the sequence end read as zeros (offset out of range); the band test drops them
+  auto dma_chunk = [&](int c) {
+    const int kc0 = kbeg + c * kChunk;
+    const uint32_t st_lds = smem_lds + (uint32_t)((c % kDqStages) * kStage);
+#pragma unroll
+    for (int i = 0; i < kDW; ++i) {
+      const int I = wave * kDW + i;
+      const int key = kc0 + rho(dma_row[i]);
+      const uint32_t voff = key < n ? (uint32_t)orig_of_key(key) * row_stride + dma_goff[i]
+                                    : lds_dma::kOutOfRange;
+      lds_dma::load16(I < kDmaMat ? rs_k : rs_v,
+                      st_lds + (I / kDmaMat) * LY::kMat + (I % kDmaMat) * 1024, voff);
+    }
+  };
+  auto load_sigma_seg = [&]() {
+    for (int i = tid; i < kSigCap; i += kThreads) {
+      const int key = seg_key0 + i;
+      sig_lds[i] = key < n ? prm.sigma[key] : INT_MAX;
+    }
+  };
+
+  // ---- prologue: sigma of the first segment, the first chunks in flight, then the columns' Q
+  // and dy rows as B operands (k step kb holds d = 16kb + 8h32 + [0, 8)), Delta and dg
+  const int seg_end0 = min(nchunks, kSegChunks);
+  if constexpr (PERM) {
+    load_sigma_seg();
+    __syncthreads();
+  }
+  for (int c = 0; c < min(kPF, seg_end0); ++c) dma_chunk(c);
+
   const int64_t rowq = ((int64_t)b * n + myorig) * prm.Hq + h;
   const char* qrow = prm.q + rowq * LY::kRowBytes;
   const char* drow = prm.dout + rowq * LY::kRowBytes;
@@ -256,54 +313,8 @@ void bwd_dq_kernel(Params prm) {
     prm.delta[rowq] = delta;
     if (prm.dgate) prm.dgate[rowq] = dot;
   }
-
-  // ---- sigma of the keys of chunks [seg_c0, seg_c0 + kSegChunks), in LDS (permuted operator)
-  int seg_c0 = 0;
-  auto load_sigma_seg = [&](int c0) {
-    const int key0 = kbeg + c0 * kChunk;
-    for (int i = tid; i < kSigCap; i += kThreads) {
-      const int key = key0 + i;
-      sig_lds[i] = key < n ? prm.sigma[key] : INT_MAX;
-    }
-  };
-  auto orig_of_key = [&](int key) { return PERM ? sig_lds[key - kbeg - seg_c0 * kChunk] : key; };
-
-  // ---- chunk staging: this thread's granules of the chunk's K and V rows, one chunk ahead
-  u32x4 st_regs[LY::kPer];
-  int st_sig = 0;
-  auto load_chunk = [&](int c) {
-    const int kc0 = kbeg + c * kChunk;
-#pragma unroll
-    for (int i = 0; i < LY::kPer; ++i) {
-      const int gi = i * kThreads + tid;
-      const int mat = gi / (kChunk * LY::kGran);
-      const int rem = gi - mat * (kChunk * LY::kGran);
-      const int row = rem / LY::kGran;
-      const int gran = rem - row * LY::kGran;
-      // keys past the end load the last key's rows (finite values; the band test drops them)
-      const int key = min(kc0 + rho(row), n - 1);
-      const int tok = orig_of_key(key);
-      st_regs[i] = *(const u32x4*)((mat ? prm.v : prm.k) +
-                                   ((((int64_t)b * n + tok) * prm.Hkv + g) * D + gran * 8) * 2);
-    }
-    if (tid < kChunk) {
-      const int key = kc0 + tid;
-      st_sig = key < n ? orig_of_key(key) : INT_MAX;
-    }
-  };
-  auto store_chunk = [&](int st) {
-    char* base = smem + st * kStage;
-#pragma unroll
-    for (int i = 0; i < LY::kPer; ++i) {
-      const int gi = i * kThreads + tid;
-      const int mat = gi / (kChunk * LY::kGran);
-      const int rem = gi - mat * (kChunk * LY::kGran);
-      const int row = rem / LY::kGran;
-      const int gran = rem - row * LY::kGran;
-      *(u32x4*)(base + mat * LY::kMat + gran_off<D>(row, gran)) = st_regs[i];
-    }
-    if (tid < kChunk) ((int*)(base + 2 * LY::kMat))[tid] = st_sig;
-  };
+  // every prologue load and store has completed (the loop counts only its own DMAs)
+  lds_dma::wait_vmcnt<0>();
 
   int k_off[LY::kKB];
 #pragma unroll
@@ -319,58 +330,67 @@ void bwd_dq_kernel(Params prm) {
 #pragma unroll
   for (int db = 0; db < LY::kDB; ++db) acc[db] = zero16();
 
-  if constexpr (PERM) {
-    load_sigma_seg(0);
-    __syncthreads();
-  }
-  load_chunk(0);
-  for (int c = 0; c < nchunks; ++c) {
-    const int st = c & 1;
-    // stage st was last read in iteration c - 2, before every wave passed barrier c - 1
-    store_chunk(st);
-    __syncthreads();
-    if (c + 1 < nchunks) {
-      if (PERM && c + 1 - seg_c0 >= kSegChunks) {
-        // every thread's sigma reads for chunk c were done before its store_chunk above
-        seg_c0 = c + 1;
-        load_sigma_seg(seg_c0);
+  // ---- chunks, segment by segment: chunk c sits in ring stage c % kDqStages
+  for (int seg_c0 = 0; seg_c0 < nchunks; seg_c0 += kSegChunks) {
+    const int seg_end = min(nchunks, seg_c0 + kSegChunks);
+    if (seg_c0 > 0) {
+      // drain the previous segment, bring in this one's sigma, then its first chunks
+      lds_dma::wait_vmcnt<0>();
+      __syncthreads();
+      seg_key0 = kbeg + seg_c0 * kChunk;
+      if constexpr (PERM) {
+        load_sigma_seg();
         __syncthreads();
       }
-      load_chunk(c + 1);
+      for (int c = seg_c0; c < min(seg_c0 + kPF, seg_end); ++c) dma_chunk(c);
     }
-    if (!wave_on || c < c_first || c > c_last) continue;
-    const char* Kst = smem + st * kStage;
-    const char* Vst = Kst + LY::kMat;
-    const int* sg = (const int*)(Kst + 2 * LY::kMat);
+    for (int c = seg_c0; c < seg_end; ++c) {
+      // chunk c has landed when at most (chunks issued after it) * kDW of this wave's DMAs are
+      // outstanding: kPF - 1 chunks in steady state, fewer near the segment end
+      const int after = min(kPF - 1, seg_end - 1 - c);
+      if (after >= 2)
+        lds_dma::wait_vmcnt<2 * kDW>();
+      else if (after == 1)
+        lds_dma::wait_vmcnt<kDW>();
+      else
+        lds_dma::wait_vmcnt<0>();
+      __syncthreads();  // every wave's DMAs of chunk c landed; chunk c - 1 is consumed
+      if (c + kPF < seg_end) dma_chunk(c + kPF);  // into chunk c - 1's stage
+      if (!wave_on || c < c_first || c > c_last) continue;
+      const char* Kst = smem + (c % kDqStages) * kStage;
+      const char* Vst = Kst + LY::kMat;
 
-    // S^T[key][col] = <K, Q>, dP^T[key][col] = <V, dy>; output register i of lane half h32 holds
-    // key 16(i / 8) + 8h32 + i % 8 of the chunk
-    f32x16 s = zero16();
-    f32x16 dp = zero16();
+      // S^T[key][col] = <K, Q>, dP^T[key][col] = <V, dy>; output register i of lane half h32
+      // holds key 16(i / 8) + 8h32 + i % 8 of the chunk
+      f32x16 s = zero16();
+      f32x16 dp = zero16();
 #pragma unroll
-    for (int kb = 0; kb < LY::kKB; ++kb) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Kst + k_off[kb]), qf[kb], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Vst + k_off[kb]), df[kb], dp, 0, 0, 0);
-    }
-    const int kc0 = kbeg + c * kChunk;
-    bf16x8 dsb[2];
+      for (int kb = 0; kb < LY::kKB; ++kb) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Kst + k_off[kb]), qf[kb], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Vst + k_off[kb]), df[kb], dp, 0, 0,
+                                                     0);
+      }
+      const int kc0 = kbeg + c * kChunk;
+      bf16x8 dsb[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int e = 16 * (r >> 3) + 8 * h32 + (r & 7);
-      const int key = kc0 + e;
-      bool ok = key >= myslot - L && key <= myslot + R && key < n;
-      if constexpr (SIGMASK) ok = ok && sg[e] <= myorig;
-      const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -lse2)) : 0.f;
-      dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gate_v, dp[r], -delta));
-    }
-    // dQ^T[d][col] += K^T[d][key] dS^T[key][col]
+      for (int r = 0; r < 16; ++r) {
+        const int e = 16 * (r >> 3) + 8 * h32 + (r & 7);
+        const int key = kc0 + e;
+        bool ok = key >= myslot - L && key <= myslot + R && key < n;
+        if constexpr (SIGMASK) ok = ok && sig_lds[key - seg_key0] <= myorig;
+        const float p =
+            ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -lse2)) : 0.f;
+        dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gate_v, dp[r], -delta));
+      }
+      // dQ^T[d][col] += K^T[d][key] dS^T[key][col]
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int db = 0; db < LY::kDB; ++db) {
-        const char* kt = Kst + 16 * t * LY::kRowBytes;
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(kt + t_off[db][0], kt + t_off[db][1]),
-                                                          dsb[t], acc[db], 0, 0, 0);
+        for (int db = 0; db < LY::kDB; ++db) {
+          const char* kt = Kst + 16 * t * LY::kRowBytes;
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_read(kt + t_off[db][0], kt + t_off[db][1]), dsb[t], acc[db], 0, 0, 0);
+        }
       }
     }
   }
