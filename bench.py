@@ -4,6 +4,8 @@
     python bench.py --nsweep      (SA against full causal attention, n = 2K .. 32K)
     python bench.py --train       (gated layer training step: forward with lse + backward)
     python bench.py --decode      (gated decode step over a KV cache, batch 128, n_max 32768)
+    python bench.py --configs     (every synthetic workload: time per layer, tokens/s, TFLOP/s,
+                                   fraction of the HBM roofline)
 
 One step is one pass of the whole hot path over one layer's synthetic input: one call of
 ssw_gated_sa_swa_forward, i.e. the SWA pass (leaves g_swa * Y_swa as the intermediate) followed by
@@ -74,6 +76,8 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="instead: one gated decode step per batch row over a KV cache")
     ap.add_argument("--batch", type=int, default=128, help="decode batch rows")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead: every synthetic workload's paths, one JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -93,6 +97,8 @@ def main():
         return train(args)
     if args.decode:
         return decode(args)
+    if args.configs:
+        return all_configs(args)
 
     wl = synth.workload(4)
     B, n, Hq, Hkv, d = wl.B, wl.n, wl.Hq, wl.Hkv, wl.d
@@ -386,6 +392,89 @@ def train(args):
         f"{bwd_ms * 1e3:.1f} us (SA path {sa_bwd_ms * 1e3:.1f}, SWA path {swa_bwd_ms * 1e3:.1f}); "
         f"backward {line['bwd_tflops']} TFLOP/s, {line['bwd_hbm_gbs']} GB/s algorithmic")
     print(json.dumps(line), flush=True)
+
+
+def all_configs(args):
+    """Every synthetic workload (synth.WORKLOADS) on its own paths and windows: per layer time,
+    tokens/s, algorithmic TFLOP/s and the fraction of the HBM roofline (algorithmic bytes of the
+    passes: each operand read once, outputs written once; the gated layer's two passes include
+    the intermediate write and read).  Each layer draws its own sigma; the Q/K/V draw of layer 0
+    is reused for the timing of every layer."""
+    import numpy as np
+    import torch
+
+    import stochastic_sliding_window_amd as ssw
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(reps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / reps
+
+    rows = []
+    for wl in synth.WORKLOADS:
+        B, n, Hq, Hkv, d = wl.B, wl.n, wl.Hq, wl.Hkv, wl.d
+        elem = 4 if wl.dtype == "f32" else 2
+        q, k, v = synth.qkv(synth.data_seed(wl.index, 0), B, n, Hq, Hkv, d, wl.dtype)
+        g = synth.gates(synth.data_seed(wl.index, 0), B, n, Hq)
+        q, k, v, g = q.to(dev), k.to(dev), v.to(dev), g.to(dev)
+        out = torch.empty_like(q)
+        sigmas = [torch.from_numpy(ssw.make_permutation(synth.sigma_seed(wl.index, l), n)).to(dev)
+                  for l in range(wl.layers)]
+        reps = 200 if n * B <= 8192 else 20
+        for w in wl.windows:
+            for causal in wl.causal_modes:
+                for path in wl.paths:
+                    ts = []
+                    for sg in sigmas:
+                        if path == "sa":
+                            fn = lambda sg=sg: ssw.sa_forward(q, k, v, sg, w, causal, out=out)
+                        elif path == "swa":
+                            fn = lambda: ssw.swa_forward(q, k, v, w, causal, out=out)
+                        else:
+                            fn = lambda sg=sg: ssw.gated_sa_swa_forward(q, k, v, sg, w, causal, g,
+                                                                        out=out)
+                        ts.append(timed(fn, reps))
+                        if path == "swa":
+                            break  # no sigma: every layer is the same computation
+                    t = float(np.mean(ts))
+                    ww = min(w, n)
+                    pairs = causal_pairs(n, ww) if causal else n * (2 * ww - 1) - ww * (ww - 1)
+                    npath = 2 if path == "gated" else 1
+                    flops = npath * 4 * d * B * Hq * pairs
+                    if path == "gated":
+                        byt = (pass_bytes(B, n, Hq, Hkv, d, elem, sa=False, accumulate=False) +
+                               pass_bytes(B, n, Hq, Hkv, d, elem, sa=True, accumulate=True))
+                    else:
+                        byt = pass_bytes(B, n, Hq, Hkv, d, elem, sa=(path == "sa"),
+                                         accumulate=False) - B * n * Hq * 4
+                    gbs = byt / (t * 1e-3) / 1e9
+                    row = {"workload": wl.name, "path": path, "window": w, "causal": causal,
+                           "dtype": wl.dtype, "layers_timed": len(ts),
+                           "us_per_layer": round(t * 1e3, 2),
+                           "tokens_per_s": round(B * n / (t * 1e-3), 1),
+                           "tflops": round(flops / (t * 1e-3) / 1e12, 2),
+                           "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+                    log(f"{wl.name} {path} w={w} causal={causal}: {row['us_per_layer']} us/layer, "
+                        f"{row['tokens_per_s'] / 1e6:.2f} M tok/s, {row['tflops']} TFLOP/s, "
+                        f"{row['hbm_gbs']} GB/s ({row['hbm_frac']:.1%} of HBM)")
+                    rows.append(row)
+        del q, k, v, g, out, sigmas
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "per-workload layer throughput (1 GPU)", "unit": "tokens/s",
+                      "higher_is_better": True, "data": "synthetic", "rows": rows}), flush=True)
 
 
 def decode(args):
