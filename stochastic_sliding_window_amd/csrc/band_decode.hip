@@ -11,9 +11,11 @@
 // head share every gathered key.  A step reads at most 2w - 1 (SA) plus w (SWA) K/V rows from
 // random cache positions, so it is bound by those row reads; it runs on the vector ALUs rather
 // than the matrix cores, which a handful of query rows would leave nearly idle.
-//   * Candidates are taken 64 at a time: their cache rows are gathered through sigma into LDS
-//     by all 256 threads (a masked candidate is redirected to row t, which is always valid, so
-//     no uninitialised cache row is ever read).
+//   * Candidates are taken 64 at a time, the SA path's chunks then the SWA path's as one
+//     sequence: their cache rows are gathered through sigma by all 256 threads (a masked
+//     candidate is redirected to row t, which is always valid, so no uninitialised cache row is
+//     ever read).  The rows of chunk c + 1 are loaded into registers, and the tokens of chunk
+//     c + 2 looked up, while chunk c is scored from LDS.
 //   * Wave v handles query heads v, v + 4, ...; for each, lane j scores candidate j against the
 //     head's query (held in LDS, read as a broadcast), the wave does the online-softmax max and
 //     sum, and lane l accumulates output elements d = kDPL * l .. kDPL * l + kDPL - 1 over the
@@ -66,7 +68,8 @@ __device__ __forceinline__ float to_f(T x) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void decode_kernel(Params prm) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void decode_kernel(Params prm) {
   constexpr int kRowBytes = D * (int)sizeof(T);
   constexpr int kGran = kRowBytes / 16;  // 16-byte granules per row
   constexpr int kDPL = D / 64;           // output elements per lane
@@ -74,8 +77,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params prm) {
   __shared__ __attribute__((aligned(16))) char k_lds[kCand * kRowBytes];
   __shared__ __attribute__((aligned(16))) char v_lds[kCand * kRowBytes];
   __shared__ __attribute__((aligned(16))) float q_lds[kMaxG * D];
-  __shared__ int tok_lds[kCand];
-  __shared__ int ok_lds[kCand];
+  __shared__ int tok_lds[2][kCand];  // chunk c's tokens in slot c % 2
+  __shared__ int ok_lds[2][kCand];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,16 +107,62 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params prm) {
   const char* vcb = prm.vc + (int64_t)b * n * prm.Hkv * kRowBytes + (int64_t)g * kRowBytes;
   const int64_t row_stride = (int64_t)prm.Hkv * kRowBytes;
 
-  for (int path = 0; path < 2; ++path) {
-    if (!((prm.paths >> path) & 1)) continue;
-    const bool sa = path == 0;
-    // candidates: SA slots [p - L, p + L], SWA positions [t - L, t]
-    const int p = sa ? prm.inv[tc] : tc;
-    const int lo = max(0, p - L);
-    const int hi = sa ? min(n - 1, p + L) : tc;
-    const int nchunks = (hi - lo) / kCand + 1;
+  // ---- the candidate chunks of both paths as one sequence: SA slots [p - L, p + L] first
+  // (chunks [0, nA)), then SWA positions [t - L, t] (chunks [nA, nA + nB))
+  const bool do_sa = prm.paths & 1;
+  const int p_sa = do_sa ? prm.inv[tc] : 0;
+  const int lo_sa = max(0, p_sa - L);
+  const int hi_sa = min(n - 1, p_sa + L);
+  const int nA = do_sa ? (hi_sa - lo_sa) / kCand + 1 : 0;
+  const int lo_w = max(0, tc - L);
+  const int nB = (prm.paths & 2) ? (tc - lo_w) / kCand + 1 : 0;
+  const int total = nA + nB;
+  // token and validity of candidate j of chunk c (masked candidates read row t, always valid)
+  auto cand = [&](int c, int j, int& tok) {
+    bool ok;
+    if (c < nA) {
+      const int q = lo_sa + c * kCand + j;
+      ok = q <= hi_sa;
+      tok = ok ? prm.sigma[q] : tc;
+      ok = ok && tok <= tc;
+    } else {
+      const int q = lo_w + (c - nA) * kCand + j;
+      ok = q <= tc;
+      tok = q;
+    }
+    if (!ok) tok = tc;
+    return ok;
+  };
 
-    float m[kMaxHW], l[kMaxHW], acc[kMaxHW][kDPL];
+  // rows of the next chunk, staged in registers while the current one is scored
+  constexpr int kPer = kCand * kGran / kThreads;  // granules per thread per matrix
+  static_assert(kPer >= 1 && kPer * kThreads == kCand * kGran, "row split");
+  u32x4 kreg[kPer], vreg[kPer];
+  auto load_rows = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int gi = i * kThreads + tid;
+      const int r = gi / kGran;
+      const int gr = gi - r * kGran;
+      const int64_t off = (int64_t)tok_lds[buf][r] * row_stride + gr * 16;
+      kreg[i] = *(const u32x4*)(kcb + off);
+      vreg[i] = *(const u32x4*)(vcb + off);
+    }
+  };
+  auto store_rows = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int gi = i * kThreads + tid;
+      const int r = gi / kGran;
+      const int gr = gi - r * kGran;
+      // K rows swizzled by granule (lane j reads row j), V rows natural
+      *(u32x4*)(k_lds + r * kRowBytes + ((gr ^ (r & (kGran - 1))) << 4)) = kreg[i];
+      *(u32x4*)(v_lds + r * kRowBytes + gr * 16) = vreg[i];
+    }
+  };
+
+  float m[kMaxHW], l[kMaxHW], acc[kMaxHW][kDPL];
+  auto reset = [&]() {
 #pragma unroll
     for (int i = 0; i < kMaxHW; ++i) {
       m[i] = -INFINITY;
@@ -121,90 +170,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params prm) {
 #pragma unroll
       for (int e = 0; e < kDPL; ++e) acc[i][e] = 0.f;
     }
-
-    for (int c = 0; c < nchunks; ++c) {
-      const int c0 = lo + c * kCand;
-      __syncthreads();  // the previous chunk's rows and tokens are no longer read
-      if (tid < kCand) {
-        const int cand = c0 + tid;
-        int tok = t;
-        bool ok = cand <= hi;
-        if (ok) {
-          tok = sa ? prm.sigma[cand] : cand;
-          ok = tok <= tc;
-        }
-        tok_lds[tid] = ok ? tok : tc;  // masked candidates read row t (always valid)
-        ok_lds[tid] = ok;
-      }
-      __syncthreads();
-      // gather: K rows swizzled by granule (lane j reads row j), V rows natural
-      for (int gi = tid; gi < kCand * kGran; gi += kThreads) {
-        const int r = gi / kGran;
-        const int gr = gi - r * kGran;
-        const int64_t off = (int64_t)tok_lds[r] * row_stride + gr * 16;
-        *(u32x4*)(k_lds + r * kRowBytes + ((gr ^ (r & (kGran - 1))) << 4)) =
-            *(const u32x4*)(kcb + off);
-        *(u32x4*)(v_lds + r * kRowBytes + gr * 16) = *(const u32x4*)(vcb + off);
-      }
-      __syncthreads();
-      const bool ok = ok_lds[lane] != 0;
-#pragma unroll
-      for (int i = 0; i < kMaxHW; ++i) {
-        if (i >= nh) break;
-        const int hh = wave + kWaves * i;
-        const float* qh = q_lds + hh * D;
-        // score of candidate `lane`
-        float s = 0.f;
-#pragma unroll
-        for (int gr = 0; gr < kGran; ++gr) {
-          const u32x4 kw = *(const u32x4*)(k_lds + lane * kRowBytes +
-                                           ((gr ^ (lane & (kGran - 1))) << 4));
-#pragma unroll
-          for (int e = 0; e < kElPerGran; ++e) {
-            float kv;
-            if constexpr (sizeof(T) == 2) {
-              const uint32_t wd = kw[e >> 1];
-              kv = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
-            } else {
-              kv = __uint_as_float(kw[e]);
-            }
-            s = __builtin_fmaf(qh[gr * kElPerGran + e], kv, s);
-          }
-        }
-        s = ok ? s * prm.scale_log2 : -INFINITY;
-        const float mx = wave_max(s);
-        const float m_new = fmaxf(m[i], mx);
-        // the candidate at row t itself is always present, so m_new is finite after its chunk;
-        // before that, with every candidate so far masked, nothing is accumulated
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[i] - m_new);
-        const float pj = ok ? __builtin_amdgcn_exp2f(s - m_new) : 0.f;
-        m[i] = m_new;
-        l[i] = l[i] * alpha + wave_sum(pj);
-#pragma unroll
-        for (int e = 0; e < kDPL; ++e) acc[i][e] *= alpha;
-        // candidate j's weight is broadcast from lane j (v_readlane into a scalar register)
-#pragma unroll 8
-        for (int j = 0; j < kCand; ++j) {
-          const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), j));
-          if constexpr (sizeof(T) == 2) {
-            if constexpr (kDPL == 2) {
-              const uint32_t wd = *(const uint32_t*)(v_lds + j * kRowBytes + 4 * lane);
-              acc[i][0] = __builtin_fmaf(pw, __uint_as_float(wd << 16), acc[i][0]);
-              acc[i][1] = __builtin_fmaf(pw, __uint_as_float(wd & 0xffff0000u), acc[i][1]);
-            } else {
-              const uint32_t hw = *(const uint16_t*)(v_lds + j * kRowBytes + 2 * lane);
-              acc[i][0] = __builtin_fmaf(pw, __uint_as_float(hw << 16), acc[i][0]);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < kDPL; ++e)
-              acc[i][e] = __builtin_fmaf(
-                  pw, *(const float*)(v_lds + j * kRowBytes + 4 * (kDPL * lane + e)), acc[i][e]);
-          }
-        }
-      }
-    }
-    // fold this path into the output: y += gate * acc / l
+  };
+  // fold a finished path into the output: y += gate * acc / l
+  auto fold = [&](int path) {
 #pragma unroll
     for (int i = 0; i < kMaxHW; ++i) {
       if (i >= nh) break;
@@ -217,6 +185,95 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params prm) {
       const float f = gv / l[i];
 #pragma unroll
       for (int e = 0; e < kDPL; ++e) y[i][e] = __builtin_fmaf(acc[i][e], f, y[i][e]);
+    }
+  };
+  reset();
+
+  // ---- prologue: chunk 0's tokens, chunk 1's tokens in registers, chunk 0's rows in registers
+  int tok_next = tc;
+  bool ok_next = false;
+  if (tid < kCand) {
+    int tk;
+    const bool ok = cand(0, tid, tk);
+    tok_lds[0][tid] = tk;
+    ok_lds[0][tid] = ok;
+    if (1 < total) ok_next = cand(1, tid, tok_next);
+  }
+  __syncthreads();
+  load_rows(0);
+
+  for (int c = 0; c < total; ++c) {
+    const int cur = c & 1;
+    const int nxt = cur ^ 1;
+    __syncthreads();  // chunk c - 1 is scored: its rows and chunk c + 1's token slot are free
+    store_rows();
+    if (tid < kCand && c + 1 < total) {
+      tok_lds[nxt][tid] = tok_next;
+      ok_lds[nxt][tid] = ok_next;
+      if (c + 2 < total) ok_next = cand(c + 2, tid, tok_next);
+    }
+    __syncthreads();
+    if (c + 1 < total) load_rows(nxt);  // in flight while chunk c is scored
+
+    const bool ok = ok_lds[cur][lane] != 0;
+#pragma unroll
+    for (int i = 0; i < kMaxHW; ++i) {
+      if (i >= nh) break;
+      const int hh = wave + kWaves * i;
+      const float* qh = q_lds + hh * D;
+      // score of candidate `lane`
+      float s = 0.f;
+#pragma unroll
+      for (int gr = 0; gr < kGran; ++gr) {
+        const u32x4 kw = *(const u32x4*)(k_lds + lane * kRowBytes +
+                                         ((gr ^ (lane & (kGran - 1))) << 4));
+#pragma unroll
+        for (int e = 0; e < kElPerGran; ++e) {
+          float kv;
+          if constexpr (sizeof(T) == 2) {
+            const uint32_t wd = kw[e >> 1];
+            kv = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+          } else {
+            kv = __uint_as_float(kw[e]);
+          }
+          s = __builtin_fmaf(qh[gr * kElPerGran + e], kv, s);
+        }
+      }
+      s = ok ? s * prm.scale_log2 : -INFINITY;
+      const float mx = wave_max(s);
+      const float m_new = fmaxf(m[i], mx);
+      // the candidate at row t itself is always present, so m_new is finite after its chunk;
+      // before that, with every candidate so far masked, nothing is accumulated
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[i] - m_new);
+      const float pj = ok ? __builtin_amdgcn_exp2f(s - m_new) : 0.f;
+      m[i] = m_new;
+      l[i] = l[i] * alpha + wave_sum(pj);
+#pragma unroll
+      for (int e = 0; e < kDPL; ++e) acc[i][e] *= alpha;
+      // candidate j's weight is broadcast from lane j (v_readlane into a scalar register)
+#pragma unroll 8
+      for (int j = 0; j < kCand; ++j) {
+        const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), j));
+        if constexpr (sizeof(T) == 2) {
+          if constexpr (kDPL == 2) {
+            const uint32_t wd = *(const uint32_t*)(v_lds + j * kRowBytes + 4 * lane);
+            acc[i][0] = __builtin_fmaf(pw, __uint_as_float(wd << 16), acc[i][0]);
+            acc[i][1] = __builtin_fmaf(pw, __uint_as_float(wd & 0xffff0000u), acc[i][1]);
+          } else {
+            const uint32_t hw = *(const uint16_t*)(v_lds + j * kRowBytes + 2 * lane);
+            acc[i][0] = __builtin_fmaf(pw, __uint_as_float(hw << 16), acc[i][0]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < kDPL; ++e)
+            acc[i][e] = __builtin_fmaf(
+                pw, *(const float*)(v_lds + j * kRowBytes + 4 * (kDPL * lane + e)), acc[i][e]);
+        }
+      }
+    }
+    if (c == nA - 1 || c == total - 1) {  // a path ends with this chunk
+      fold(c < nA ? 0 : 1);
+      reset();
     }
   }
 
