@@ -17,6 +17,7 @@ definitions on the pages:
   query row at a time), the rows' log-sum-exp, and sampled-row forms for large n.
 * decode.py      -- one decode step over a KV cache (row t of causal SA over the full context).
 * coverage.py    -- receptive-field growth over layers (sets, small n).
+* gates.py       -- the gate projections g = sigmoid(x w + b) of the gated layer.
 
 Sources (the pages):
   [SA-ja] "技術的概要：確率的アテンション" (gist.science/ja/paper/2604.00754) -- Stochastic
@@ -53,6 +54,7 @@ from .backward import (
 )
 from .decode import sa_decode, swa_decode, gated_decode
 from .coverage import coverage_by_layer
+from .gates import gate_projection
 
 __all__ = [
     "splitmix64_stream",
@@ -77,4 +79,5 @@ __all__ = [
     "swa_decode",
     "gated_decode",
     "coverage_by_layer",
+    "gate_projection",
 ]
