@@ -6,6 +6,7 @@
     python bench.py --decode      (gated decode step over a KV cache, batch 128, n_max 32768)
     python bench.py --configs     (every synthetic workload: time per layer, tokens/s, TFLOP/s,
                                    fraction of the HBM roofline)
+    python bench.py --gates       (gate projections sigmoid(x w + b), n 32768, Hm 4096, 32 heads)
 
 One step is one pass of the whole hot path over one layer's synthetic input: one call of
 ssw_gated_sa_swa_forward, i.e. the SWA pass (leaves g_swa * Y_swa as the intermediate) followed by
@@ -78,6 +79,8 @@ def main():
     ap.add_argument("--batch", type=int, default=128, help="decode batch rows")
     ap.add_argument("--configs", action="store_true",
                     help="instead: every synthetic workload's paths, one JSON line")
+    ap.add_argument("--gates", action="store_true",
+                    help="instead: the gate projections of the long-context layer")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -99,6 +102,8 @@ def main():
         return decode(args)
     if args.configs:
         return all_configs(args)
+    if args.gates:
+        return gates_bench(args)
 
     wl = synth.workload(4)
     B, n, Hq, Hkv, d = wl.B, wl.n, wl.Hq, wl.Hkv, wl.d
@@ -475,6 +480,47 @@ def all_configs(args):
         torch.cuda.empty_cache()
     print(json.dumps({"metric": "per-workload layer throughput (1 GPU)", "unit": "tokens/s",
                       "higher_is_better": True, "data": "synthetic", "rows": rows}), flush=True)
+
+
+def gates_bench(args):
+    """ssw_gate_projection on the long-context layer's tokens: x [32768, 4096] bf16 (a hidden size
+    of 4096), 32 query heads (64 outputs).  HBM roofline on x read once plus the gates written."""
+    import torch
+
+    import stochastic_sliding_window_amd as ssw
+    import synth
+
+    rows, Hm, Hq = 32768, 4096, 32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    x, w_t, bias = synth.gate_inputs(synth.data_seed(4, 0), rows, Hm, Hq)
+    xs = [x.to(dev) for _ in range(3)]  # rotated so no call finds x in the last-level cache
+    w_t, bias = w_t.to(dev), bias.to(dev)
+    out = torch.empty(2, rows, Hq, dtype=torch.float32, device=dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    for i in range(5):
+        ssw.gate_projection(xs[i % 3], w_t, bias, out=out)
+    torch.cuda.synchronize()
+    K = 60
+    start.record(stream)
+    for i in range(K):
+        ssw.gate_projection(xs[i % 3], w_t, bias, out=out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t = start.elapsed_time(end) / K
+    byt = rows * Hm * 2 + 2 * Hq * Hm * 2 + 2 * rows * Hq * 4
+    gbs = byt / (t * 1e-3) / 1e9
+    line = {"metric": "gate projections sigmoid(x w + b) (1 GPU)", "unit": "us",
+            "value": round(t * 1e3, 2), "higher_is_better": False, "dtype": "bf16",
+            "data": "synthetic", "config": {"rows": rows, "Hm": Hm, "Hq": Hq},
+            "tflops": round(2 * rows * Hm * 2 * Hq / (t * 1e-3) / 1e12, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "bytes_per_launch": byt}}
+    log(f"gate projection {rows}x{Hm} -> 2x{Hq}: {t * 1e3:.1f} us, {gbs:.0f} GB/s")
+    print(json.dumps(line), flush=True)
 
 
 def decode(args):

@@ -128,6 +128,22 @@ int ssw_gated_sa_swa_forward_ex(const void* q, const void* k, const void* v, con
                                 int causal, const float* gates, void* out, int B, int n, int Hq,
                                 int Hkv, int d, int dtype, void* stream);
 
+/* ---- Gate projections of the gated layer ----
+ *
+ * [SA-ja] ゲート付き SA と SWA の組み合わせ computes g_sa and g_swa by independent sigmoid
+ * projections of the layer input.  This call computes both in one pass over x:
+ *     gates[p][r][h] = sigmoid(sum_k x[r][k] * w_t[p * Hq + h][k] + bias[p * Hq + h])
+ * for path p (0: SA, 1: SWA), token row r (= b * n + i) and query head h, directly in the
+ * [2, B, n, Hq] layout ssw_gated_sa_swa_forward takes.
+ *   x      device bf16 [rows, Hm], 16-byte aligned; Hm a multiple of 16.
+ *   w_t    device bf16 [2 * Hq, Hm] (a linear layer's weight layout: one row per output),
+ *          16-byte aligned; 1 <= Hq <= 64.
+ *   bias   device float32 [2 * Hq] or NULL.
+ *   gates  device float32 [2, rows, Hq], overwritten.
+ * fp32 accumulation; bf16 only (SSW_EDTYPE otherwise). */
+int ssw_gate_projection(const void* x, const void* w_t, const float* bias, float* gates, int rows,
+                        int Hm, int Hq, int dtype, void* stream);
+
 /* ---- Training: forward with the rows' log-sum-exp, backward, gated forward and backward ----
  *
  * The pages pretrain a model from scratch with the gated layer ([SA-ja] 主要な貢献 item 3 and

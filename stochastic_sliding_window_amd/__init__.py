@@ -27,6 +27,10 @@ Variant: one sigma per batch row and/or KV head (sigma [B, n], [Hkv, n] or [B, H
     sa_forward_ex(q, k, v, sigmas, window, causal, gate=None, out=None)
     gated_sa_swa_forward_ex(q, k, v, sigmas, window, causal, gates, out=None)
 
+Gate projections (g = sigmoid(x w_t^T + b) into the [2, B, n, Hq] gates layout):
+
+    gate_projection(x, w_t, bias=None, Hq=None, out=None)
+
 Decode (one new token per batch row over a KV cache):
 
     sa_decode(q, k_cache, v_cache, sigma, inv_sigma, pos, window, gate=None, out=None)
@@ -56,7 +60,7 @@ __all__ = [
     "last_error", "F32", "BF16", "sa_forward_lse", "swa_forward_lse", "sa_backward",
     "swa_backward", "gated_sa_swa_forward_train", "gated_sa_swa_backward", "sa_decode",
     "swa_decode", "gated_sa_swa_decode", "sa_forward_ex", "gated_sa_swa_forward_ex",
-    "receptive_field_coverage",
+    "receptive_field_coverage", "gate_projection",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -124,6 +128,8 @@ def _load() -> ctypes.CDLL:
         fn.argtypes = [vp, vp, vp, i32p, i64, i64, i32, i32, f32p, vp, i32, i32, i32, i32, i32,
                        i32, vp]
         fn.restype = ctypes.c_int
+    lib.ssw_gate_projection.argtypes = [vp, vp, f32p, f32p, i32, i32, i32, i32, vp]
+    lib.ssw_gate_projection.restype = ctypes.c_int
     lib.ssw_receptive_field_coverage.argtypes = [i32, i32, i32, vp, i32, i32, vp]
     lib.ssw_receptive_field_coverage.restype = ctypes.c_int
     lib.ssw_make_permutation.argtypes = [ctypes.c_uint64, i32, i32p, i32p]
@@ -588,4 +594,36 @@ def gated_sa_swa_forward_ex(q, k, v, sigmas, window: int, causal: bool, gates, o
                                             sb, sh, int(window), int(bool(causal)), _dev_ptr(gates),
                                             _dev_ptr(out), B, n, Hq, k.shape[2], d, _dtype_code(q),
                                             _stream_handle(q)))
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# gate projections
+# ------------------------------------------------------------------------------------------
+
+def gate_projection(x, w_t, bias=None, out=None):
+    """gates [2, *x.shape[:-1], Hq] = sigmoid(x @ w_t.T + bias) (ssw_gate_projection).
+
+    x: bf16 [..., Hm] (e.g. [B, n, Hm]); w_t: bf16 [2 Hq, Hm]; bias: float32 [2 Hq] or None.
+    """
+    torch = _torch()
+    for name, t in (("x", x), ("w_t", w_t)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous device tensor")
+    if w_t.dim() != 2 or w_t.shape[1] != x.shape[-1] or w_t.shape[0] % 2:
+        raise ValueError("w_t must be [2 * Hq, Hm] with Hm = x.shape[-1]")
+    Hq = w_t.shape[0] // 2
+    lead = tuple(x.shape[:-1])
+    rows = int(np.prod(lead)) if lead else 1
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (2 * Hq,) or
+                             not bias.is_contiguous() or bias.device != x.device):
+        raise ValueError("bias must be a contiguous float32 [2 * Hq] tensor on x's device")
+    if out is None:
+        out = torch.empty((2, *lead, Hq), dtype=torch.float32, device=x.device)
+    else:
+        out = _prep_rows(out, (2, *lead, Hq), torch.float32, x.device, "out")
+    if x.dtype != torch.bfloat16 or w_t.dtype != torch.bfloat16:
+        raise TypeError("x and w_t must be bfloat16")
+    _check(_lib.ssw_gate_projection(_dev_ptr(x), _dev_ptr(w_t), _dev_ptr(bias), _dev_ptr(out),
+                                    rows, x.shape[-1], Hq, BF16, _stream_handle(x)))
     return out

@@ -28,7 +28,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["ssw_api.cpp", "band_attn.hip", "band_attn_bwd.hip", "band_decode.hip"]
+SOURCES = ["ssw_api.cpp", "band_attn.hip", "band_attn_bwd.hip", "band_decode.hip", "gate_proj.hip"]
 
 
 def hipcc() -> str:

@@ -15,6 +15,7 @@
 
 #include "../../include/ssw.h"
 #include "band_attn.h"
+#include "gate_proj.h"
 
 namespace {
 
@@ -557,6 +558,31 @@ int ssw_gated_sa_swa_decode(const void* q, const void* k_cache, const void* v_ca
                             int Hkv, int d, int dtype, void* stream) {
   return decode("ssw_gated_sa_swa_decode", q, k_cache, v_cache, sigma, inv_sigma, pos, window,
                 gates, out, B, n_max, Hq, Hkv, d, dtype, stream, 3);
+}
+
+// ---- gate projections of the gated layer
+
+int ssw_gate_projection(const void* x, const void* w_t, const float* bias, float* gates, int rows,
+                        int Hm, int Hq, int dtype, void* stream) {
+  const char* who = "ssw_gate_projection";
+  if (rows < 0 || Hm < 1 || Hq < 1)
+    return fail(SSW_EINVAL, std::string(who) + ": need rows >= 0, Hm >= 1 and Hq >= 1");
+  if (dtype != SSW_BF16) return fail(SSW_EDTYPE, std::string(who) + ": bf16 x and w_t only");
+  if (Hm % 16 != 0 || Hq > 64)
+    return fail(SSW_ESHAPE, std::string(who) + ": Hm must be a multiple of 16 and Hq <= 64");
+  if ((int64_t)rows * Hm * 2 > ((int64_t)1 << 40))
+    return fail(SSW_ESHAPE, std::string(who) + ": x too large");
+  if (rows == 0) return SSW_OK;
+  if (!x || !w_t || !gates)
+    return fail(SSW_EINVAL, std::string(who) + ": x, w_t and gates must be non-NULL");
+  if (!aligned(x, 16) || !aligned(w_t, 16) || !aligned(gates, 4) || (bias && !aligned(bias, 4)))
+    return fail(SSW_EALIGN, std::string(who) + ": x and w_t must be 16-byte aligned, gates and "
+                                               "bias 4-byte aligned");
+  hipError_t e = ssw::launch_gate_projection(x, w_t, bias, gates, rows, Hm, Hq,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess)
+    return fail(SSW_EHIP, std::string(who) + ": kernel launch failed: " + hipGetErrorString(e));
+  return SSW_OK;
 }
 
 int ssw_make_permutation(uint64_t seed, int n, int32_t* sigma_out, int32_t* inv_out) {

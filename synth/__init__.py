@@ -98,3 +98,13 @@ def upstream_grad(seed: int, B: int, n: int, Hq: int, d: int, dtype: str = "bf16
     """
     g = torch.Generator().manual_seed(seed ^ 0x3C3C)
     return torch.randn(B, n, Hq, d, generator=g, dtype=torch.float32).to(_DT[dtype])
+
+
+def gate_inputs(seed: int, rows: int, Hm: int, Hq: int):
+    """Layer input x [rows, Hm] ~ N(0, 1) (bf16), projection weight w_t [2 Hq, Hm] ~ N(0, 1/Hm)
+    (bf16, so each logit is ~ N(0, 1)) and bias [2 Hq] ~ N(0, 1) (fp32), CPU tensors."""
+    g = torch.Generator().manual_seed(seed ^ 0x6B6B)
+    x = torch.randn(rows, Hm, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    w_t = (torch.randn(2 * Hq, Hm, generator=g, dtype=torch.float32) / Hm ** 0.5).to(torch.bfloat16)
+    bias = torch.randn(2 * Hq, generator=g, dtype=torch.float32)
+    return x, w_t, bias

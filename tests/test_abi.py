@@ -298,3 +298,16 @@ def test_strided_sigma_checks():
         assert f(*args(sig=P + 2)) == -4
     assert _lib.ssw_gated_sa_swa_forward_ex(P, P, P, P, 0, 0, 8, 1, None, P, 1, 64, 4, 2, 64, 1,
                                             None) == -1
+
+
+def test_gate_projection_checks():
+    f = _lib.ssw_gate_projection
+    f.argtypes = [_VP] * 4 + [_I] * 4 + [_VP]
+    f.restype = _I
+    assert f(P, P, None, P, -1, 64, 4, 1, None) == -1
+    assert f(P, P, None, P, 10, 64, 4, 0, None) == -3
+    assert f(P, P, None, P, 10, 40, 4, 1, None) == -2       # Hm not a multiple of 16
+    assert f(P, P, None, P, 10, 64, 65, 1, None) == -2      # Hq > 64
+    assert f(None, P, None, P, 10, 64, 4, 1, None) == -1
+    assert f(P + 8, P, None, P, 10, 64, 4, 1, None) == -4
+    assert f(P, P, None, P, 0, 64, 4, 1, None) == 0
