@@ -9,10 +9,11 @@
 //
 // Mapping onto the chip: a skinny GEMM (N = 2 Hq <= 128 columns, K = Hm) bound by reading x.  A
 // workgroup takes 128 rows, a wave 32 of them; each wave accumulates its 32 x N tile with bf16
-// 32x32x16 MFMAs, reading its x rows (A operands, 16 bytes per lane per k step) and the
-// projection's rows w_t[j] (B operands; w_t is [N, Hm] row-major, the usual layout of a linear
-// layer's weight) straight from memory, four k steps at a time so the loads of the next are in
-// flight.  The epilogue adds the bias, applies the sigmoid and scatters the columns to their
+// 32x32x16 MFMAs.  Its x rows are read row-contiguously in blocks of 64 k, one block ahead, and
+// staged through a wave-private LDS buffer into the A-operand layout; the projection's rows
+// w_t[j] (B operands; w_t is [N, Hm] row-major, the usual layout of a linear layer's weight) are
+// read straight from memory (they stay in the L2).  A split of the k range over the waves of a
+// workgroup (4x the waves in flight) measured slower: every workgroup then reads all of w_t.  The epilogue adds the bias, applies the sigmoid and scatters the columns to their
 // gate plane.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,6 +42,7 @@ struct Params {
 
 template <int NT>
 __global__ __launch_bounds__(kThreads) void gate_proj_kernel(Params prm) {
+  __shared__ __attribute__((aligned(16))) char x_lds[4][32 * 128];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r32 = lane & 31;
@@ -65,6 +67,47 @@ __global__ __launch_bounds__(kThreads) void gate_proj_kernel(Params prm) {
   // holds column 32t + r32 at the same k
   const int steps = prm.Hm / 16;
   int s = 0;
+  // Blocks of 64 k: the wave's 32 x rows are read row-contiguously (8 lanes cover a row's
+  // 128 bytes), one block ahead in registers, and go through a wave-private LDS buffer (granules
+  // XOR-swizzled by row) from which the A operands are read.
+  {
+    char* xl = x_lds[wave];
+    const int nblk = prm.Hm / 64;
+    const char* xwave = prm.x + (int64_t)row0 * rb;
+    auto load_blk = [&](int kb, u32x4 (&r)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = min(8 * i + lane / 8, prm.rows - 1 - row0);
+        r[i] = *(const u32x4*)(xwave + (int64_t)row * rb + kb * 128 + (lane % 8) * 16);
+      }
+    };
+    u32x4 cur[4], nxt[4];
+    if (nblk > 0) load_blk(0, cur);
+    for (int kb = 0; kb < nblk; ++kb) {
+      if (kb + 1 < nblk) load_blk(kb + 1, nxt);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * i + lane / 8;
+        *(u32x4*)(xl + row * 128 + ((((lane % 8) ^ (row & 7))) << 4)) = cur[i];
+      }
+      // the wave's own LDS stores precede its reads (in-order LDS queue); nothing else shares
+      // this buffer
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 a = *(const u32x4*)(xl + r32 * 128 + (((2 * u + h32) ^ (r32 & 7)) << 4));
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, a),
+              __builtin_bit_cast(bf16x8, *(const u32x4*)(wrow[t] + 32 * (4 * kb + u))), acc[t],
+              0, 0, 0);
+      }
+      if (kb + 1 < nblk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+    }
+    s = 4 * nblk;
+  }
   for (; s + kUnroll <= steps; s += kUnroll) {
     u32x4 a[kUnroll], bw[kUnroll][NT];
 #pragma unroll
