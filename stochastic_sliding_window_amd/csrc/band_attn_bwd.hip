@@ -420,9 +420,15 @@ template <int D, bool PERM, bool SIGMASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(Params prm) {
   using LY = Lay<D>;
-  // per stage: Q rows, dy rows, then per column log2-domain lse, Delta, gate, slot, original index
+  // per stage: Q rows, dy rows, then per column lse, Delta, gate (64 floats each: a 4-byte DMA
+  // covers 64 lanes), slot, original index
   constexpr int kMetaOff = 2 * LY::kMat;
-  constexpr int kStage = kMetaOff + 5 * kChunk * 4;
+  constexpr int kStage = kMetaOff + 3 * 64 * 4 + 2 * kChunk * 4;
+  constexpr int kSlotOff = kMetaOff + 3 * 64 * 4;
+  constexpr int kRowsPerDma = 1024 / LY::kRowBytes;
+  constexpr int kDmaMat = LY::kMat / 1024;  // DMA instructions per matrix and chunk
+  constexpr int kDW = 2 * kDmaMat / 4;      // per wave
+  static_assert(kDW >= 1 && 2 * kDmaMat == 4 * kDW, "DMA split");
   constexpr int kVOff = 2 * kStage;                      // V rows of the 128 keys
   constexpr int kSigOff = kVOff + kTile * LY::kRowBytes;
   __shared__ __attribute__((aligned(16))) char smem[kSigOff + (PERM ? kSigCap * 4 : 0)];
@@ -486,71 +492,63 @@ void bwd_dkdv_kernel(Params prm) {
   };
   auto orig_of_slot = [&](int slot) { return PERM ? sig_lds[slot - seg_s0] : slot; };
 
-  // ---- chunk staging: Q and dy rows of 32 query columns plus their per-column values
-  u32x4 st_regs[LY::kPer];
-  float m_lse2 = 0.f, m_delta = 0.f, m_gate = 0.f;
-  int m_slot = 0, m_orig = 0;
-  auto load_chunk = [&](int c) {
+  // ---- chunk staging: direct buffer-to-LDS loads of the chunk's Q and dy rows (MFMA row order,
+  // granules XOR-swizzled by row) and of its columns' lse, Delta and gate; the slot and original
+  // index of each column are written by the first 32 threads.  One chunk is in flight while the
+  // previous one is scored (two stages: the V rows of the tile take the rest of the LDS).
+  const uint32_t smem_lds = lds_dma::lds_addr(smem);
+  const int64_t qd_batch = (int64_t)b * n * prm.Hq;
+  const uint32_t qd_range = (uint32_t)((int64_t)n * prm.Hq * LY::kRowBytes);
+  const lds_dma::i32x4 rs_q = lds_dma::resource(prm.q + qd_batch * LY::kRowBytes, qd_range);
+  const lds_dma::i32x4 rs_d = lds_dma::resource(prm.dout + qd_batch * LY::kRowBytes, qd_range);
+  const uint32_t m_range = (uint32_t)((int64_t)n * prm.Hq * 4);
+  const lds_dma::i32x4 rs_m = lds_dma::resource(
+      wave == 0 ? (const void*)(prm.lse + qd_batch)
+                : wave == 1 ? (const void*)(prm.delta + qd_batch)
+                            : (const void*)(prm.gate ? prm.gate + qd_batch : prm.lse + qd_batch),
+      m_range);
+  // row of column c0 + e within batch row b: token row * Hq + query head
+  auto col_row = [&](int slot0, int rem0, int e, int& slot) {
+    const int x = rem0 + e;
+    const int ds = div_small(x, prm.inv_g);
+    slot = slot0 + ds;
+    return orig_of_slot(slot) * prm.Hq + g * G + (x - ds * G);
+  };
+  auto dma_chunk = [&](int c) {
     const int c0 = col_lo + c * kChunk;
     const int slot0 = c0 / G;  // wave-uniform
     const int rem0 = c0 - slot0 * G;
+    const uint32_t st_lds = smem_lds + (uint32_t)((c & 1) * kStage);
 #pragma unroll
-    for (int i = 0; i < LY::kPer; ++i) {
-      const int gi = i * kThreads + tid;
-      const int mat = gi / (kChunk * LY::kGran);
-      const int rem = gi - mat * (kChunk * LY::kGran);
-      const int row = rem / LY::kGran;
-      const int gran = rem - row * LY::kGran;
-      // columns past the end load the last column's rows (finite values; their band test fails)
-      const int x = min(rem0 + rho(row), nG - 1 - slot0 * G);
-      const int ds = div_small(x, prm.inv_g);
-      const int tok = orig_of_slot(slot0 + ds);
-      st_regs[i] = *(const u32x4*)((mat ? prm.dout : prm.q) +
-                                   ((((int64_t)b * n + tok) * prm.Hq + g * G + (x - ds * G)) * D +
-                                    gran * 8) * 2);
+    for (int i = 0; i < kDW; ++i) {
+      const int I = wave * kDW + i;
+      const int row = kRowsPerDma * (I % kDmaMat) + lane / LY::kGran;
+      const int e = rho(row);
+      int slot;
+      uint32_t voff = lds_dma::kOutOfRange;
+      if (c0 + e < nG)  // columns past the end read as zeros; their band test fails
+        voff = (uint32_t)col_row(slot0, rem0, e, slot) * LY::kRowBytes +
+               (uint32_t)((((lane % LY::kGran) ^ (row & (LY::kGran - 1)))) << 4);
+      lds_dma::load16(I < kDmaMat ? rs_q : rs_d,
+                      st_lds + (I / kDmaMat) * LY::kMat + (I % kDmaMat) * 1024, voff);
+    }
+    // waves 0, 1, 2 fetch lse, Delta, gate (lanes 0..31: the chunk's columns)
+    if (wave < 3 && (wave < 2 || prm.gate)) {
+      int slot;
+      uint32_t moff = lds_dma::kOutOfRange;
+      if (lane < kChunk && c0 + lane < nG) moff = (uint32_t)col_row(slot0, rem0, lane, slot) * 4u;
+      lds_dma::load4(rs_m, st_lds + kMetaOff + wave * 256, moff);
     }
     if (tid < kChunk) {
-      const int col = c0 + tid;
-      if (col < nG) {
-        const int x = rem0 + tid;
-        const int ds = div_small(x, prm.inv_g);
-        const int slot = slot0 + ds;
-        const int tok = orig_of_slot(slot);
-        const int64_t row = ((int64_t)b * n + tok) * prm.Hq + g * G + (x - ds * G);
-        m_lse2 = prm.lse[row] * kLog2e;
-        m_delta = prm.delta[row];
-        m_gate = prm.gate ? prm.gate[row] : 1.0f;
-        m_slot = slot;
-        m_orig = tok;
+      int* mi = (int*)(smem + (c & 1) * kStage + kSlotOff);
+      if (c0 + tid < nG) {
+        const int ds = div_small(rem0 + tid, prm.inv_g);
+        mi[tid] = slot0 + ds;
+        mi[kChunk + tid] = orig_of_slot(slot0 + ds);  // the column's token: its original index
       } else {
-        // no key passes the band test (q <= slot + R fails) or the causal test
-        m_lse2 = 0.f;
-        m_delta = 0.f;
-        m_gate = 0.f;
-        m_slot = INT_MIN / 4;
-        m_orig = -1;
+        mi[tid] = INT_MIN / 4;  // no key passes the band test (q <= slot + R fails)
+        mi[kChunk + tid] = -1;
       }
-    }
-  };
-  auto store_chunk = [&](int st) {
-    char* base = smem + st * kStage;
-#pragma unroll
-    for (int i = 0; i < LY::kPer; ++i) {
-      const int gi = i * kThreads + tid;
-      const int mat = gi / (kChunk * LY::kGran);
-      const int rem = gi - mat * (kChunk * LY::kGran);
-      const int row = rem / LY::kGran;
-      const int gran = rem - row * LY::kGran;
-      *(u32x4*)(base + mat * LY::kMat + gran_off<D>(row, gran)) = st_regs[i];
-    }
-    if (tid < kChunk) {
-      float* mf = (float*)(base + kMetaOff);
-      int* mi = (int*)(base + kMetaOff);
-      mf[tid] = m_lse2;
-      mf[kChunk + tid] = m_delta;
-      mf[2 * kChunk + tid] = m_gate;
-      mi[3 * kChunk + tid] = m_slot;
-      mi[4 * kChunk + tid] = m_orig;
     }
   };
 
@@ -575,26 +573,26 @@ void bwd_dkdv_kernel(Params prm) {
     load_sigma_seg(seg_s0);
     __syncthreads();
   }
-  load_chunk(0);
+  dma_chunk(0);
   for (int c = 0; c < nchunks; ++c) {
     const int st = c & 1;
-    store_chunk(st);
-    __syncthreads();
+    lds_dma::wait_vmcnt<0>();  // this wave's loads of chunk c (and, first time, the prologue's)
+    __syncthreads();           // every wave's; chunk c - 1 is scored, its stage is free
     if (c + 1 < nchunks) {
       const int last_slot = min(n - 1, (col_lo + (c + 2) * kChunk - 1) / G);
       if (PERM && last_slot - seg_s0 >= kSigCap) {
-        // every thread's sigma reads for chunk c were done before its store_chunk above
+        // every read of the current segment (chunk c's loads) was before the barrier above
         seg_s0 = (col_lo + (c + 1) * kChunk) / G;
         load_sigma_seg(seg_s0);
         __syncthreads();
       }
-      load_chunk(c + 1);
+      dma_chunk(c + 1);
     }
     if (!wave_on || c < c_first || c > c_last) continue;
     const char* Qst = smem + st * kStage;
     const char* Dst = Qst + LY::kMat;
-    const float* mf = (const float*)(Qst + kMetaOff);
-    const int* mi = (const int*)(Qst + kMetaOff);
+    const float* mf = (const float*)(Qst + kMetaOff);  // lse [0, 64), Delta [64, ..), gate
+    const int* mi = (const int*)(Qst + kSlotOff);        // slot [0, 32), original index [32, 64)
 
     // S[col][key] = <Q, K>, dP[col][key] = <dy, V>; output register i of lane half h32 holds
     // column 16(i / 8) + 8h32 + i % 8 of the chunk, for the lane's key
@@ -610,14 +608,15 @@ void bwd_dkdv_kernel(Params prm) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int e = 16 * (r >> 3) + 8 * h32 + (r & 7);
-      const int slot = mi[3 * kChunk + e];
+      const int slot = mi[e];
       bool ok = myk >= slot - L && myk <= slot + R;
-      if constexpr (SIGMASK) ok = ok && ktok <= mi[4 * kChunk + e];
-      const float p =
-          ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -mf[e])) : 0.f;
-      const float gt = mf[2 * kChunk + e];
+      if constexpr (SIGMASK) ok = ok && ktok <= mi[kChunk + e];
+      const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2,
+                                                                 -mf[e] * kLog2e))
+                         : 0.f;
+      const float gt = prm.gate ? mf[128 + e] : 1.0f;
       pb[r >> 3][r & 7] = (__bf16)(p * gt);
-      dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gt, dp[r], -mf[kChunk + e]));
+      dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gt, dp[r], -mf[64 + e]));
     }
     // dV^T[d][key] += dy^T[d][col] (g P)[col][key];  dK^T[d][key] += Q^T[d][col] dS[col][key]
 #pragma unroll
