@@ -552,16 +552,6 @@ void bwd_dkdv_kernel(Params prm) {
     }
   };
 
-  int a_off[LY::kKB];
-#pragma unroll
-  for (int kb = 0; kb < LY::kKB; ++kb) a_off[kb] = gran_off<D>(r32, 2 * kb + h32);
-  int t_off[LY::kDB][2];
-#pragma unroll
-  for (int db = 0; db < LY::kDB; ++db) {
-    t_off[db][0] = tr_off<D>(lane, db, 0);
-    t_off[db][1] = tr_off<D>(lane, db, 1);
-  }
-
   f32x16 dk[LY::kDB], dv[LY::kDB];
 #pragma unroll
   for (int db = 0; db < LY::kDB; ++db) {
@@ -591,6 +581,19 @@ void bwd_dkdv_kernel(Params prm) {
     if (!wave_on || c < c_first || c > c_last) continue;
     const char* Qst = smem + st * kStage;
     const char* Dst = Qst + LY::kMat;
+    // The per-lane LDS offsets are recomputed here from a lane index the optimiser cannot see
+    // through (so it cannot hoist them out of the loop): holding them would spill registers.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    int a_off[LY::kKB];
+#pragma unroll
+    for (int kb = 0; kb < LY::kKB; ++kb) a_off[kb] = gran_off<D>(ln & 31, 2 * kb + (ln >> 5));
+    int t_off[LY::kDB][2];
+#pragma unroll
+    for (int db = 0; db < LY::kDB; ++db) {
+      t_off[db][0] = tr_off<D>(ln, db, 0);
+      t_off[db][1] = tr_off<D>(ln, db, 1);
+    }
     const float* mf = (const float*)(Qst + kMetaOff);  // lse [0, 64), Delta [64, ..), gate
     const int* mi = (const int*)(Qst + kSlotOff);        // slot [0, 32), original index [32, 64)
 
