@@ -67,7 +67,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--window", type=int, default=128)
-    ap.add_argument("--sweep", action="store_true", help="also time SA / SWA alone at w 32, 64, 128")
+    ap.add_argument("--sweep", action="store_true", help="also time SA / SWA alone at w 16 .. 512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size (0 = auto)")
     ap.add_argument("--nsweep", action="store_true",
@@ -189,7 +189,7 @@ def main():
 
     sweep = {}
     if args.sweep:
-        for ww in (32, 64, 128):
+        for ww in (16, 32, 64, 128, 256, 512):
             for name in ("sa", "swa"):
                 def run(s, ww=ww, name=name):
                     if name == "sa":

@@ -1058,33 +1058,37 @@ void band_attn_kernel(Params prm) {
 
   // ---- epilogue: normalise, gate, scatter to original row sigma[p]
   const float l_tot = pair_sum(l_run);
-  if (!colvalid) return;
+  if (!wave_on) return;
   // The row's log-sum-exp for a backward pass.  Every row holds its own token, so m_ref is finite
   // and l_tot >= 1 here; l_tot sums exp2 of the scaled scores minus m_ref.
-  if (prm.lse && h32 == 0)
+  if (prm.lse && h32 == 0 && colvalid)
     prm.lse[((int64_t)b * n + myorig) * prm.Hq + h] =
         (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   const float f = __builtin_amdgcn_rcpf(l_tot) * gate_v;
-  char* orow = prm.out + qrow_elems * (int64_t)sizeof(T);
-  const char* prow = nullptr;  // this column's prefetched intermediate row (LDS)
-  if constexpr (kPrefetchPartial) {
-    wait_vmcnt<0>();
+  if constexpr (kBf16) {
+    // The wave's 32 finished rows are assembled in its own 8 KB of LDS: a ring stage that the
+    // last loop step does not read (the slice the gated SA pass prefetched its intermediate rows
+    // into), same swizzled row layout.  Each lane turns its register fragments into 16-bit words
+    // in place; the rows then leave as whole 16-byte granules, kGran lanes per row, so a store
+    // instruction writes 64 / kGran complete rows instead of 16 bytes of each of 32 rows.
     const int segc_last = nchunks - (nseg - 1) * kSegChunks;
-    prow = smem + partial_region((segc_last - 1) % Lay::kNS) + (lane & 31) * Lay::kRowBytes;
-  }
+    char* reg = smem + partial_region((segc_last - 1) % Lay::kNS);
+    char* rowp = reg + (lane & 31) * Lay::kRowBytes;
+    if constexpr (kPrefetchPartial) wait_vmcnt<0>();
 #pragma unroll
-  for (int t = 0; t < kOT; ++t) {
+    for (int t = 0; t < kOT; ++t) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int d0 = 32 * t + 8 * a + 4 * h32;
-      float y[4];
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * t + 8 * a + 4 * h32;
+        // granule d0 / 8 of the row, swizzled by column; bytes 8 * h32 within it
+        u32x2* slot = (u32x2*)(rowp + 16 * ((d0 >> 3) ^ ((lane & 31) & (Lay::kGran - 1))) +
+                               8 * h32);
+        float y[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) y[u] = o[t][4 * a + u] * f;
-      if constexpr (kBf16) {
-        u32x2* dst = (u32x2*)(orow + d0 * 2);
+        for (int u = 0; u < 4; ++u) y[u] = o[t][4 * a + u] * f;
+        uint32_t w[2];
         if constexpr (EPI == kEpiPartial) {
           // the gated intermediate: fp16 of y * 2^-8 (8x finer than bf16, range 1.6e7)
-          uint32_t w[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const _Float16 lo = (_Float16)(y[2 * u] * kPartialScale);
@@ -1092,17 +1096,11 @@ void band_attn_kernel(Params prm) {
             w[u] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                    ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
           }
-          *dst = u32x2{w[0], w[1]};
         } else {
           if constexpr (EPI == kEpiAddPartial) {
-            u32x2 old;
-            if constexpr (kPrefetchPartial) {
-              // granule d0 / 8 of the row, swizzled by column; bytes 8 * h32 within it
-              const int gsw = ((d0 >> 3) ^ ((lane & 31) & (Lay::kGran - 1)));
-              old = *(const u32x2*)(prow + 16 * gsw + 8 * h32);
-            } else {
-              old = *dst;  // not prefetched: read the intermediate where it lies
-            }
+            const u32x2 old = kPrefetchPartial ? *slot : *(const u32x2*)(prm.out +
+                                  (int64_t)b * out_batch_bytes + (colvalid ? out_off : 0u) +
+                                  d0 * 2);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
               y[2 * u] += (float)__builtin_bit_cast(_Float16, (uint16_t)(old[u] & 0xffffu)) *
@@ -1111,13 +1109,38 @@ void band_attn_kernel(Params prm) {
                               kPartialUnscale;
             }
           }
-          const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[0]) |
-                              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[1]) << 16);
-          const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[2]) |
-                              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[3]) << 16);
-          *dst = u32x2{w0, w1};
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            w[u] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[2 * u]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[2 * u + 1]) << 16);
         }
-      } else {
+        *slot = u32x2{w[0], w[1]};
+      }
+    }
+    // the rows are read back by other lanes of this wave: its LDS writes must have completed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    char* obatch = prm.out + (int64_t)b * out_batch_bytes;
+    constexpr int kRowsPerStore = 64 / Lay::kGran;
+#pragma unroll
+    for (int i = 0; i < 32 / kRowsPerStore; ++i) {
+      const int r = i * kRowsPerStore + lane / Lay::kGran;  // wave-relative column
+      const int gran = lane % Lay::kGran;
+      const uint32_t roff = (uint32_t)__builtin_amdgcn_ds_bpermute(r * 4, (int)out_off);
+      const u32x4 v =
+          *(const u32x4*)(reg + r * Lay::kRowBytes + 16 * (gran ^ (r & (Lay::kGran - 1))));
+      if (roff != kOutOfRange) *(u32x4*)(obatch + roff + 16 * gran) = v;
+    }
+  } else {
+    if (!colvalid) return;
+    char* orow = prm.out + qrow_elems * (int64_t)sizeof(T);
+#pragma unroll
+    for (int t = 0; t < kOT; ++t) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * t + 8 * a + 4 * h32;
+        float y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) y[u] = o[t][4 * a + u] * f;
         // fp32: the gated intermediate is plain fp32
         f32x4* dst = (f32x4*)(orow + d0 * 4);
         if constexpr (EPI == kEpiAddPartial) {
