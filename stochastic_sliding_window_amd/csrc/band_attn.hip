@@ -934,9 +934,10 @@ void band_attn_kernel(Params prm) {
             const bool hb = ca + 1 < segc;
             const bool fetch_a = ca + 2 < segc;
             const bool fetch_b = ca + 3 < segc;
-            DmaRows ra, rb;
-            if (fetch_a) ra = dma_prep(seg_key0 + (ca + 2) * kChunk, seg_key0);
-            if (fetch_b) rb = dma_prep(seg_key0 + (ca + 3) * kChunk, seg_key0);
+            // rows of the next step's chunks (read for a chunk inside the segment even when
+            // nothing is fetched, so that the row registers need no other definition)
+            const DmaRows ra = dma_prep(seg_key0 + min(ca + 2, segc - 1) * kChunk, seg_key0);
+            const DmaRows rb = dma_prep(seg_key0 + min(ca + 3, segc - 1) * kChunk, seg_key0);
             wait_vmcnt<0>();  // this step's chunks (the only loads in flight)
             __syncthreads();  // and every wave's; the previous step's slots are free
             if (fetch_a)
