@@ -40,6 +40,7 @@ namespace bwd {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define SSW_LDS __attribute__((address_space(3)))
@@ -113,17 +114,56 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
-// Store four consecutive values of a gradient row (8 bytes), adding the stored ones if asked.
-__device__ __forceinline__ void store4(char* p, float y0, float y1, float y2, float y3, bool add) {
-  u32x2* dst = (u32x2*)p;
-  if (add) {
-    const u32x2 old = *dst;
-    y0 += bf_lo(old[0]);
-    y1 += bf_hi(old[0]);
-    y2 += bf_lo(old[1]);
-    y3 += bf_hi(old[1]);
+// A wave's 32 gradient rows, from MFMA fragments to memory.  Lane l holds row l % 32; register
+// 4a + u of block db holds element d = 32db + 8a + 4(l / 32) + u.  The rows are assembled in fp32
+// in the wave's 32 * D * 4 bytes of LDS at `reg` (16-byte granules XOR-swizzled by row), then
+// leave as whole 16-byte bf16 granules, D / 8 lanes per row, so that one store instruction writes
+// complete rows.  Row r goes to base + (row offset held by lane r); lanes holding kOutOfRange
+// have no row.  `accumulate` adds the stored row in fp32 and rounds once.
+template <int D>
+__device__ __forceinline__ void store_rows(char* reg, const f32x16* acc, float scale, char* base,
+                                           uint32_t my_off, bool accumulate, int lane) {
+  constexpr int kG32 = D / 4;  // 16-byte fp32 granules per row
+  const int r32 = lane & 31;
+  const int h32 = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int gi = (8 * db + 2 * a + h32) ^ (r32 & (kG32 - 1));
+      *(f32x4*)(reg + r32 * D * 4 + 16 * gi) =
+          f32x4{acc[db][4 * a] * scale, acc[db][4 * a + 1] * scale, acc[db][4 * a + 2] * scale,
+                acc[db][4 * a + 3] * scale};
+    }
   }
-  *dst = u32x2{pack2(y0, y1), pack2(y2, y3)};
+  // the rows are read back by other lanes of this wave: its LDS writes must have completed
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerRound = 64 / kLanesPerRow;
+#pragma unroll
+  for (int i = 0; i < 32 / kRowsPerRound; ++i) {
+    const int r = i * kRowsPerRound + lane / kLanesPerRow;
+    const int j = lane % kLanesPerRow;  // elements 8j .. 8j + 7
+    const uint32_t roff = (uint32_t)__builtin_amdgcn_ds_bpermute(r * 4, (int)my_off);
+    const char* src = reg + r * D * 4;
+    const f32x4 lo = *(const f32x4*)(src + 16 * ((2 * j) ^ (r & (kG32 - 1))));
+    const f32x4 hi = *(const f32x4*)(src + 16 * ((2 * j + 1) ^ (r & (kG32 - 1))));
+    if (roff != lds_dma::kOutOfRange) {
+      u32x4* dst = (u32x4*)(base + roff + 16 * j);
+      float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (accumulate) {
+        const u32x4 old = *dst;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[2 * e] += bf_lo(old[e]);
+          y[2 * e + 1] += bf_hi(old[e]);
+        }
+      }
+      *dst = u32x4{pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7])};
+    }
+  }
+  // the wave's LDS slice may be written again right after (reads done before any later write)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 template <int D>
@@ -395,19 +435,17 @@ void bwd_dq_kernel(Params prm) {
     }
   }
 
-  // ---- epilogue: dQ row of the column at its original token; register 4a + u of block db holds
-  // d = 32db + 8a + 4h32 + u
-  if (!colvalid) return;
-  char* dqrow = prm.dq + rowq * LY::kRowBytes;
-#pragma unroll
-  for (int db = 0; db < LY::kDB; ++db) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int d0 = 32 * db + 8 * a + 4 * h32;
-      store4(dqrow + 2 * d0, acc[db][4 * a] * prm.scale, acc[db][4 * a + 1] * prm.scale,
-             acc[db][4 * a + 2] * prm.scale, acc[db][4 * a + 3] * prm.scale, prm.accumulate != 0);
-    }
-  }
+  // ---- epilogue: dQ row of the column at its original token, assembled in fp32 in the ring
+  // (free once every wave is past its last chunk: each wave takes 32 rows)
+  __syncthreads();
+  static_assert(4 * 32 * D * 4 <= kSigOff, "fp32 rows of four waves fit the ring");
+  if (!wave_on) return;
+  // byte offset of the column's dQ row within batch row b (below 2^31, checked at the API)
+  const uint32_t my_off =
+      colvalid ? (uint32_t)(((int64_t)myorig * prm.Hq + h) * LY::kRowBytes) : lds_dma::kOutOfRange;
+  store_rows<D>(smem + wave * 32 * D * 4, acc, prm.scale,
+                prm.dq + (int64_t)b * n * prm.Hq * LY::kRowBytes, my_off, prm.accumulate != 0,
+                lane);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -636,22 +674,18 @@ void bwd_dkdv_kernel(Params prm) {
     }
   }
 
-  // ---- epilogue: dK and dV rows of the lane's key at its original token
-  if (!keyvalid) return;
-  char* dkrow = prm.dk + krow * LY::kRowBytes;
-  char* dvrow = prm.dv + krow * LY::kRowBytes;
-  const bool add = prm.accumulate != 0;
-#pragma unroll
-  for (int db = 0; db < LY::kDB; ++db) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int d0 = 32 * db + 8 * a + 4 * h32;
-      store4(dkrow + 2 * d0, dk[db][4 * a] * prm.scale, dk[db][4 * a + 1] * prm.scale,
-             dk[db][4 * a + 2] * prm.scale, dk[db][4 * a + 3] * prm.scale, add);
-      store4(dvrow + 2 * d0, dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2],
-             dv[db][4 * a + 3], add);
-    }
-  }
+  // ---- epilogue: dK, then dV, rows of the lane's key at its original token, each assembled in
+  // fp32 in LDS (the stages and the V rows are free once every wave is past its last chunk)
+  __syncthreads();
+  static_assert(4 * 32 * D * 4 <= kSigOff, "fp32 rows of four waves fit the stages and V rows");
+  if (!wave_on) return;
+  // byte offset of the key's row within batch row b (below 2^31, checked at the API)
+  const uint32_t my_off =
+      keyvalid ? (uint32_t)(((int64_t)ktok * prm.Hkv + g) * LY::kRowBytes) : lds_dma::kOutOfRange;
+  const int64_t kv_batch = (int64_t)b * n * prm.Hkv * LY::kRowBytes;
+  char* reg = smem + wave * 32 * D * 4;
+  store_rows<D>(reg, dk, prm.scale, prm.dk + kv_batch, my_off, prm.accumulate != 0, lane);
+  store_rows<D>(reg, dv, 1.0f, prm.dv + kv_batch, my_off, prm.accumulate != 0, lane);
 }
 
 // ------------------------------------------------------------------------------------------------
