@@ -399,16 +399,22 @@ void band_attn_kernel(Params prm) {
     return ((last_stage + 1 + wave / 2) % Lay::kNS) * Lay::kStageBytes +
            (wave % 2) * Lay::kMatBytes;
   };
-  auto dma_partial = [&](int last_stage, uint32_t my_out_off) {
+  // Whole rows of the wave's 32 columns from a [B, n, Hq, D] tensor (the intermediate in `out`,
+  // or Q: both have that layout, so a column's row offset is out_off for either) into the
+  // wave's 8 KB region next to ring slot last_stage.
+  auto dma_rows = [&](const i32x4& rsrc, int last_stage, uint32_t my_row_off) {
     const uint32_t region = smem_lds + partial_region(last_stage);
     constexpr int kColsPerDma = 1024 / Lay::kRowBytes;
 #pragma unroll
     for (int i = 0; i < Lay::kDmaK; ++i) {
       const int c = i * kColsPerDma + lane / Lay::kGran;  // wave-relative column
-      const uint32_t base = (uint32_t)__builtin_amdgcn_ds_bpermute(c * 4, (int)my_out_off);
+      const uint32_t base = (uint32_t)__builtin_amdgcn_ds_bpermute(c * 4, (int)my_row_off);
       const int gran = (lane % Lay::kGran) ^ (c & (Lay::kGran - 1));
-      dma16(rs_out, __builtin_amdgcn_readfirstlane(region + 1024 * i), base + 16 * gran);
+      dma16(rsrc, __builtin_amdgcn_readfirstlane(region + 1024 * i), base + 16 * gran);
     }
+  };
+  auto dma_partial = [&](int last_stage, uint32_t my_out_off) {
+    dma_rows(rs_out, last_stage, my_out_off);
   };
   // After a sigma segment has landed (and a barrier): the entries of keys past the sequence end
   // (read as 0 by the buffer range check) become n, so their K/V rows fall outside the buffers.
@@ -434,8 +440,15 @@ void band_attn_kernel(Params prm) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if constexpr (PERM) patch_sigma_tail(kbeg, min(nchunks, kSegChunks));
-  // the first chunks of the first segment go in flight before Q is loaded, so the two overlap
-  static_for<kPro>([&](auto pf) {
+  // bf16: the wave's Q rows come in as whole rows by the same LDS DMA as K and V (one
+  // instruction per 1 KB of contiguous rows instead of 32-byte pieces of 32 rows), into ring
+  // slots that are free until the loop starts: kQSt slots hold the workgroup's rows, in the
+  // region layout the epilogue uses.  The first kProEarly chunks go in flight before Q so the
+  // loads overlap; with a 3-slot ring the remaining prologue chunk follows once Q has been read.
+  constexpr int kQSt = (kWaves + 1) / 2;
+  constexpr bool kQDma = kBf16 && Lay::kNS - 1 >= kQSt;
+  constexpr int kProEarly = kQDma ? (kPro < Lay::kNS - kQSt ? kPro : Lay::kNS - kQSt) : kPro;
+  static_for<kProEarly>([&](auto pf) {
     if (pf() < min(nchunks, kSegChunks)) dma_chunk(kbeg + pf() * kChunk, pf, kbeg);
   });
 
@@ -449,7 +462,27 @@ void band_attn_kernel(Params prm) {
   constexpr int kQRegs = kBf16 ? D / 16 : D / 2;
   typedef typename std::conditional<kBf16, bf16x8, float>::type QFrag;
   QFrag qf[kQRegs];
-  if constexpr (kBf16) {
+  if constexpr (kQDma) {
+    const i32x4 rs_q = make_rsrc(prm.q + (int64_t)b * out_batch_bytes, (uint32_t)out_batch_bytes);
+    dma_rows(rs_q, kProEarly - 1, out_off);
+    wait_vmcnt<0>();
+    // column c's granule g sits at c * kRowBytes + 16 * (g ^ (c % kGran)); the B operand of
+    // the score MFMA for d block kb is granule 2 kb + h32
+    const int c = lane & 31;
+    const char* qreg = smem + partial_region(kProEarly - 1) + c * Lay::kRowBytes;
+#pragma unroll
+    for (int kb = 0; kb < kQRegs; ++kb)
+      qf[kb] = __builtin_bit_cast(
+          bf16x8, *(const u32x4*)(qreg + 16 * ((2 * kb + h32) ^ (c & (Lay::kGran - 1)))));
+    if constexpr (kProEarly < kPro) {
+      __syncthreads();  // every wave has read its Q rows before the next chunk overwrites them
+      static_for<kPro - kProEarly>([&](auto pf) {
+        constexpr int kC = kProEarly + decltype(pf)::value;
+        if (kC < min(nchunks, kSegChunks))
+          dma_chunk(kbeg + kC * kChunk, std::integral_constant<int, kC>{}, kbeg);
+      });
+    }
+  } else if constexpr (kBf16) {
     const char* qp = prm.q + (qrow_elems + 8 * h32) * 2;
 #pragma unroll
     for (int kb = 0; kb < kQRegs; ++kb) {
