@@ -1155,10 +1155,14 @@ void band_attn_kernel(Params prm) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     char* obatch = prm.out + (int64_t)b * out_batch_bytes;
     constexpr int kRowsPerStore = 64 / Lay::kGran;
+    // the lane index is made opaque here so that the row indices below are recomputed: shared
+    // with the identical ones of the prologue's Q row fetch, they stayed live across the loop
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
 #pragma unroll
     for (int i = 0; i < 32 / kRowsPerStore; ++i) {
-      const int r = i * kRowsPerStore + lane / Lay::kGran;  // wave-relative column
-      const int gran = lane % Lay::kGran;
+      const int r = i * kRowsPerStore + lane_e / Lay::kGran;  // wave-relative column
+      const int gran = lane_e % Lay::kGran;
       const uint32_t roff = (uint32_t)__builtin_amdgcn_ds_bpermute(r * 4, (int)out_off);
       const u32x4 v =
           *(const u32x4*)(reg + r * Lay::kRowBytes + 16 * (gran ^ (r & (Lay::kGran - 1))));
