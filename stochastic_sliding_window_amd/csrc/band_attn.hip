@@ -94,8 +94,17 @@ constexpr int kStages = SSW_STAGES;  // LDS ring depth: kStages - 1 chunks in fl
 #ifndef SSW_SIGCAP
 #define SSW_SIGCAP 2048
 #endif
+// SA alone (sigma-gathered, plain store epilogue) has a second build for three waves per SIMD
+// with a 3-slot ring and a 1024-entry sigma segment (3 x 16 KB + 4 KB of LDS per workgroup at
+// bf16/d128, so three workgroups fit a CU).  It is launched when the workgroup's band fits one
+// sigma segment; longer bands use the two-wave build, which holds 2048 entries.
+#ifndef SSW_W3_STORE
+#define SSW_W3_STORE 1
+#endif
+#ifndef SSW_SIGCAP_W3
+#define SSW_SIGCAP_W3 1024
+#endif
 constexpr int kSigCap = SSW_SIGCAP;  // sigma entries held in LDS at a time
-constexpr int kSegChunks = kSigCap / kChunk;
 constexpr float kLazy = 8.0f;  // reference max may lag the true max by up to 2^8 (log2 units)
 // bf16 gated path: the SWA pass leaves g_swa * Y_swa in the output buffer as fp16 scaled by 2^-8
 constexpr float kPartialScale = 1.0f / 256.0f;
@@ -109,6 +118,13 @@ __device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int,
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// x, as a value the compiler cannot see through: a lane-derived value passed through this at its
+// use is recomputed there instead of being hoisted out of the loop into a register of its own.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -189,7 +205,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <typename T, int D, bool PERM>
+template <typename T, int D, bool PERM, bool W3 = false>
 struct Layout {
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int kRowBytes = D * (int)sizeof(T);
@@ -200,9 +216,11 @@ struct Layout {
   static constexpr int kDmaPerWave = 2 * kDmaK / kWaves;
   static constexpr int kStageBytes = 2 * kMatBytes;
   // sigma of a segment of keys (permuted operator only)
-  static constexpr int kSigBytes = PERM ? kSigCap * 4 : 0;
+  static constexpr int kSigCapL = W3 ? SSW_SIGCAP_W3 : kSigCap;
+  static constexpr int kSegChunks = kSigCapL / kChunk;
+  static constexpr int kSigBytes = PERM ? kSigCapL * 4 : 0;
   // ring depth: the configured number of stages, or fewer if they would not fit in 160 KB of LDS
-  static constexpr int kWant = PERM ? kStages : SSW_STAGES_SWA;
+  static constexpr int kWant = W3 ? 3 : PERM ? kStages : SSW_STAGES_SWA;
   static constexpr int kNS = kWant * kStageBytes + kSigBytes <= 163840
                                  ? kWant
                                  : (163840 - kSigBytes) / kStageBytes;
@@ -265,16 +283,39 @@ __device__ __forceinline__ int xcd_local_order(int i, int nblocks) {
   return i;
 }
 
-template <typename T, bool PERM>
-constexpr int kWavesPerEU = (PERM || sizeof(T) != 2) ? SSW_WPE : SSW_WPE_SWA;
+template <typename T, bool PERM, int EPI, bool W3>
+constexpr bool kIsW3 = W3 && PERM && sizeof(T) == 2 && EPI == kEpiStore;
+template <typename T, bool PERM, int EPI, bool W3>
+constexpr int kWavesPerEU =
+    kIsW3<T, PERM, EPI, W3> ? 3 : (PERM || sizeof(T) != 2) ? SSW_WPE : SSW_WPE_SWA;
 
-template <typename T, int D, bool PERM, bool SIGMASK, int EPI>
+template <typename T, int D, bool PERM, bool SIGMASK, int EPI, bool W3>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kWavesPerEU<T, PERM>, kWavesPerEU<T, PERM>)))
+__attribute__((amdgpu_waves_per_eu(kWavesPerEU<T, PERM, EPI, W3>,
+                                   kWavesPerEU<T, PERM, EPI, W3>)))
 void band_attn_kernel(Params prm) {
-  using Lay = Layout<T, D, PERM>;
-  constexpr bool kPipe = PERM ? SSW_PIPELINE : SSW_PIPELINE_SWA;
+  constexpr bool kW3 = kIsW3<T, PERM, EPI, W3>;
+  using Lay = Layout<T, D, PERM, kW3>;
+  constexpr int kSegChunks = Lay::kSegChunks;  // chunks per sigma segment
+  constexpr bool kPipe = kW3 ? false : PERM ? SSW_PIPELINE : SSW_PIPELINE_SWA;
   constexpr bool kBf16 = Lay::kBf16;
+  // At three waves per SIMD (168 registers) the causal sigma-gathered kernel recomputes some
+  // lane constants at their use instead of holding them across the loop: the DMA row keys and
+  // offsets, the K/V LDS offsets (one base register each), and it reads sigma for the causal
+  // mask in two halves.
+  constexpr bool kLeanAny = kW3 && SIGMASK;
+#ifndef SSW_LEAN_DMA
+#define SSW_LEAN_DMA 1
+#endif
+#ifndef SSW_LEAN_KV
+#define SSW_LEAN_KV 1
+#endif
+#ifndef SSW_LEAN_MASK
+#define SSW_LEAN_MASK 1
+#endif
+  constexpr bool kLeanDma = kLeanAny && SSW_LEAN_DMA;
+  constexpr bool kLean = kLeanAny && SSW_LEAN_KV;  // K/V LDS offsets
+  constexpr bool kLeanMask = kLeanAny && SSW_LEAN_MASK;
   __shared__ __attribute__((aligned(16))) char smem[Lay::kSmem];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;  // LDS byte address of smem
   int* sig_lds = (int*)(smem + Lay::kSigOff);
@@ -338,17 +379,30 @@ void band_attn_kernel(Params prm) {
   // this lane fetches and the byte offset of its (swizzled) source granule
   constexpr int kDW = Lay::kDmaPerWave;
   const uint32_t row_stride32 = (uint32_t)kv_row_stride;
-  int dma_key[kDW];
-  uint32_t dma_goff[kDW];
-#pragma unroll
-  for (int i = 0; i < kDW; ++i) {
+  // row of instruction i: kRowsPerDma * blkid + lane / kGran, source granule lane % kGran
+  auto dma_key_of = [&](int i, int ln) -> int {
     const int I = wave * kDW + i;  // wave-uniform
     const bool isv = I >= Lay::kDmaK;
     const int blkid = isv ? I - Lay::kDmaK : I;
-    const int row = blkid * Lay::kRowsPerDma + lane / Lay::kGran;
-    const int gran = lane % Lay::kGran;
-    dma_key[i] = isv ? row : row_to_key(row);
-    dma_goff[i] = (uint32_t)((gran ^ (isv ? swz_v<Lay::kGran>(row) : swz_k<Lay::kGran>(row))) * 16);
+    const int row = blkid * Lay::kRowsPerDma + ln / Lay::kGran;
+    return isv ? row : row_to_key(row);
+  };
+  auto dma_goff_of = [&](int i, int ln) -> uint32_t {
+    const int I = wave * kDW + i;
+    const bool isv = I >= Lay::kDmaK;
+    const int blkid = isv ? I - Lay::kDmaK : I;
+    const int row = blkid * Lay::kRowsPerDma + ln / Lay::kGran;
+    const int gran = ln % Lay::kGran;
+    return (uint32_t)((gran ^ (isv ? swz_v<Lay::kGran>(row) : swz_k<Lay::kGran>(row))) * 16);
+  };
+  int dma_key[kLeanDma ? 1 : kDW];
+  uint32_t dma_goff[kLeanDma ? 1 : kDW];
+  if constexpr (!kLeanDma) {
+#pragma unroll
+    for (int i = 0; i < kDW; ++i) {
+      dma_key[i] = dma_key_of(i, lane);
+      dma_goff[i] = dma_goff_of(i, lane);
+    }
   }
   // STAGE is a compile-time ring slot, so LDS addresses fold into instruction offsets.  The sigma
   // reads for all of this wave's rows go out first (unconditionally: the segment's sigma buffer
@@ -360,7 +414,7 @@ void band_attn_kernel(Params prm) {
     DmaRows r;
 #pragma unroll
     for (int i = 0; i < kDW; ++i) {
-      const int q = kc0 + dma_key[i];
+      const int q = kc0 + (kLeanDma ? dma_key_of(i, opaque(lane)) : dma_key[i]);
       r.row[i] = PERM ? sig_lds[q - seg_key0] : q;
     }
     return r;
@@ -375,7 +429,8 @@ void band_attn_kernel(Params prm) {
       const int I = wave * kDW + i;  // wave-uniform
       const bool isv = I >= Lay::kDmaK;
       const int blkid = isv ? I - Lay::kDmaK : I;
-      const uint32_t voff = __umul24((uint32_t)r.row[i], row_stride32) + dma_goff[i];
+      const uint32_t voff = __umul24((uint32_t)r.row[i], row_stride32) +
+                            (kLeanDma ? dma_goff_of(i, opaque(lane)) : dma_goff[i]);
       const uint32_t lds = smem_lds + STAGE * Lay::kStageBytes + (isv ? Lay::kMatBytes : 0) +
                            blkid * 1024;
       dma16(isv ? rs_v : rs_k, __builtin_amdgcn_readfirstlane(lds), voff);
@@ -516,25 +571,39 @@ void band_attn_kernel(Params prm) {
   // ---- per-lane LDS offsets of the MFMA operands within a stage (the same for every chunk)
   const int r32 = lane & 31;
   constexpr int kKReads = kBf16 ? D / 16 : D / 8;  // 16-byte K reads per chunk
-  int k_off[kKReads];
+  int k_off[kLean ? 1 : kKReads];
+  if constexpr (!kLean) {
 #pragma unroll
-  for (int u = 0; u < kKReads; ++u) {
-    const int gran = kBf16 ? 2 * u + h32 : h32 * (D / 8) + u;
-    k_off[u] = r32 * Lay::kRowBytes + ((gran ^ swz_k<Lay::kGran>(r32)) << 4);
+    for (int u = 0; u < kKReads; ++u) {
+      const int gran = kBf16 ? 2 * u + h32 : h32 * (D / 8) + u;
+      k_off[u] = r32 * Lay::kRowBytes + ((gran ^ swz_k<Lay::kGran>(r32)) << 4);
+    }
   }
+  // kLean: the offset of d block u is k_base ^ (u << 5) (the granule 2u + h32 is XOR-swizzled
+  // with r32 % kGran, and the u part of (2u + h32) ^ (r32 % kGran) lands in bits 5.. of the
+  // offset); one opaque copy of k_base per chunk keeps the eight offsets out of registers.
+  const int k_base = r32 * Lay::kRowBytes + ((h32 ^ swz_k<Lay::kGran>(r32)) << 4);
+  // offset of K d block u given kbv = opaque(k_base) (kLean) or anything (otherwise)
+  auto k_at = [&](int kbv, int u) -> int {
+    if constexpr (kLean)
+      return kbv ^ (u << 5);
+    else
+      return k_off[u];
+  };
   // bf16: transposed V reads.  Lane j of 16-lane group grp reads 4 d-values of key
   // 16t + 8*h32 + j/4 (+4 for the upper half) at d = 32db + 16(grp%2) + 4(j%4); the tr16 read then
   // hands lane i of the group column i, i.e. the A operand row d = 32db + lane%32.  Key % 4 (and
   // so the swizzle) is the same for every (t, half), which only add 16t + 4*half rows: one base
   // offset per d block, the rest are instruction offsets.
-  int v_off[kOT];
+  // kLean: v_off[db] = v_off[0] ^ (db << 6) (the d block enters the granule index as 4 db)
+  int v_off[kLean ? 1 : kOT];
   if constexpr (kBf16) {
     const int grp = lane >> 4;
     const int j = lane & 15;
     const int dsub = 16 * (grp & 1) + 4 * (j & 3);
     const int key = 8 * h32 + (j >> 2);
 #pragma unroll
-    for (int db = 0; db < kOT; ++db) {
+    for (int db = 0; db < (kLean ? 1 : kOT); ++db) {
       const int d = 32 * db + dsub;
       v_off[db] = Lay::kMatBytes + key * Lay::kRowBytes +
                   (((d >> 3) ^ swz_v<Lay::kGran>(key)) << 4) + ((d & 7) << 1);
@@ -548,9 +617,10 @@ void band_attn_kernel(Params prm) {
     const char* Kst = smem + STAGE * Lay::kStageBytes;
     f32x16 s = zero16();
     if constexpr (kBf16) {
+      const int kbv = kLean ? opaque(k_base) : 0;
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kst + k_off[kb]));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kst + k_at(kbv, kb)));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s, 0, 0, 0);
       }
     } else {
@@ -662,11 +732,13 @@ void band_attn_kernel(Params prm) {
       }
       l_run = l_run * alpha + psum;
       const SSW_LDS char* vbase = (const SSW_LDS char*)Kst;
+      const int vbv = kLean ? opaque(v_off[0]) : 0;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int db = 0; db < kOT; ++db) {
-          const SSW_LDS char* vp = vbase + v_off[db] + 16 * t * Lay::kRowBytes;
+          const int vo = kLean ? (vbv ^ (db << 6)) : v_off[db];
+          const SSW_LDS char* vp = vbase + vo + 16 * t * Lay::kRowBytes;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)vp);
           const s16x4 hi =
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)(vp + 4 * Lay::kRowBytes));
@@ -715,45 +787,82 @@ void band_attn_kernel(Params prm) {
       const char* Kst = smem + STAGE * Lay::kStageBytes;
       const char* Kn = smem + (NEXT >= 0 ? NEXT : 0) * Lay::kStageBytes;
 
-      // mask.  Register r holds key kc0 + 16(r/8) + 8*h32 + r%8.  The causal test folds into a
-      // 16-bit mask as sigma is read, so no sigma value stays live in a register.
-      uint32_t cm = 0xFFFFu;
-      if constexpr (SIGMASK) {
+      float sm[16];
+      if constexpr (kLeanMask && SIGMASK) {
+        // Register r holds key kc0 + 16(r/8) + 8*h32 + r%8.  sigma is read and applied in two
+        // halves of 8 keys, with a scheduling barrier between them, so that at most 8 sigma
+        // values are live; an edge chunk also tests the lane's band bits.
         const int* sp = sig_lds + (kc0 - seg_key0);
-        cm = 0u;
+        uint32_t band16 = 0xFFFFu;
+        if (!interior) {
+          const int a = max(max(myslot - L, 0) - kc0, 0);
+          const int z = min(min(myslot + R, n - 1) - kc0, 31);
+          const uint32_t upto = z < 0 ? 0u : (0xFFFFFFFFu >> (31 - z));
+          const uint32_t from = a > 31 ? 0u : (0xFFFFFFFFu << a);
+          const uint32_t bm = (upto & from) >> (8 * h32);
+          band16 = (bm & 0xFFu) | ((bm >> 8) & 0xFF00u);
+        }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const u32x4 a = *(const u32x4*)(sp + 16 * half + 8 * h32);
-          const u32x4 bq = *(const u32x4*)(sp + 16 * half + 8 * h32 + 4);
+          const u32x4 a4 = *(const u32x4*)(sp + 16 * half + 8 * h32);
+          const u32x4 b4 = *(const u32x4*)(sp + 16 * half + 8 * h32 + 4);
+          if (interior) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            cm |= (uint32_t)((int)a[e] <= myorig) << (8 * half + e);
-            cm |= (uint32_t)((int)bq[e] <= myorig) << (8 * half + 4 + e);
+            for (int e = 0; e < 4; ++e) {
+              sm[8 * half + e] = (int)a4[e] <= myorig ? s[8 * half + e] : -INFINITY;
+              sm[8 * half + 4 + e] = (int)b4[e] <= myorig ? s[8 * half + 4 + e] : -INFINITY;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r0 = 8 * half + e, r1 = 8 * half + 4 + e;
+              sm[r0] = ((int)a4[e] <= myorig && ((band16 >> r0) & 1u)) ? s[r0] : -INFINITY;
+              sm[r1] = ((int)b4[e] <= myorig && ((band16 >> r1) & 1u)) ? s[r1] : -INFINITY;
+            }
+          }
+          if (half == 0) __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        // mask.  Register r holds key kc0 + 16(r/8) + 8*h32 + r%8.  The causal test folds into a
+        // 16-bit mask as sigma is read, so no sigma value stays live in a register.
+        uint32_t cm = 0xFFFFu;
+        if constexpr (SIGMASK) {
+          const int* sp = sig_lds + (kc0 - seg_key0);
+          cm = 0u;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const u32x4 a = *(const u32x4*)(sp + 16 * half + 8 * h32);
+            const u32x4 bq = *(const u32x4*)(sp + 16 * half + 8 * h32 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              cm |= (uint32_t)((int)a[e] <= myorig) << (8 * half + e);
+              cm |= (uint32_t)((int)bq[e] <= myorig) << (8 * half + 4 + e);
+            }
           }
         }
-      }
-      float sm[16];
-      if (interior) {
+        if (interior) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm[r] = ((cm >> r) & 1u) ? s[r] : -INFINITY;
-      } else {
-        const int a = max(max(myslot - L, 0) - kc0, 0);
-        const int z = min(min(myslot + R, n - 1) - kc0, 31);
-        const uint32_t upto = z < 0 ? 0u : (0xFFFFFFFFu >> (31 - z));
-        const uint32_t from = a > 31 ? 0u : (0xFFFFFFFFu << a);
-        const uint32_t bm = (upto & from) >> (8 * h32);
-        // band bit of register r is bit 16(r/8) + r%8 of bm; keep both tests in one mask
-        const uint32_t band16 = (bm & 0xFFu) | ((bm >> 8) & 0xFF00u);
-        const uint32_t all = band16 & cm;
+          for (int r = 0; r < 16; ++r) sm[r] = ((cm >> r) & 1u) ? s[r] : -INFINITY;
+        } else {
+          const int a = max(max(myslot - L, 0) - kc0, 0);
+          const int z = min(min(myslot + R, n - 1) - kc0, 31);
+          const uint32_t upto = z < 0 ? 0u : (0xFFFFFFFFu >> (31 - z));
+          const uint32_t from = a > 31 ? 0u : (0xFFFFFFFFu << a);
+          const uint32_t bm = (upto & from) >> (8 * h32);
+          // band bit of register r is bit 16(r/8) + r%8 of bm; keep both tests in one mask
+          const uint32_t band16 = (bm & 0xFFu) | ((bm >> 8) & 0xFF00u);
+          const uint32_t all = band16 & cm;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm[r] = ((all >> r) & 1u) ? s[r] : -INFINITY;
+          for (int r = 0; r < 16; ++r) sm[r] = ((all >> r) & 1u) ? s[r] : -INFINITY;
+        }
       }
 
       // scores of the next chunk, interleaved with the column max and the first weights
       if constexpr (NEXT >= 0) {
+        const int kbv = kLean ? opaque(k_base) : 0;
 #pragma unroll
         for (int kb = 0; kb < D / 16; ++kb) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kn + k_off[kb]));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kn + k_at(kbv, kb)));
           sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], sn, 0, 0, 0);
         }
       }
@@ -793,11 +902,13 @@ void band_attn_kernel(Params prm) {
       }
       l_run = l_run * alpha + psum;
       const SSW_LDS char* vbase = (const SSW_LDS char*)Kst;
+      const int vbv = kLean ? opaque(v_off[0]) : 0;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int db = 0; db < kOT; ++db) {
-          const SSW_LDS char* vp = vbase + v_off[db] + 16 * t * Lay::kRowBytes;
+          const int vo = kLean ? (vbv ^ (db << 6)) : v_off[db];
+          const SSW_LDS char* vp = vbase + vo + 16 * t * Lay::kRowBytes;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)vp);
           const s16x4 hi =
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)(vp + 4 * Lay::kRowBytes));
@@ -859,15 +970,16 @@ void band_attn_kernel(Params prm) {
       const char* Ka = smem + STA * Lay::kStageBytes;
       const char* Kb = smem + (STA + 1) * Lay::kStageBytes;
       f32x16 s_a = zero16(), s_b = zero16();
+      const int kbv = kLean ? opaque(k_base) : 0;
 #pragma unroll
       for (int kb = 0; kb < D / 16; ++kb) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Ka + k_off[kb]));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Ka + k_at(kbv, kb)));
         s_a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s_a, 0, 0, 0);
       }
       if (hb) {
 #pragma unroll
         for (int kb = 0; kb < D / 16; ++kb) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kb + k_off[kb]));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kb + k_at(kbv, kb)));
           s_b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s_b, 0, 0, 0);
         }
       }
@@ -916,7 +1028,8 @@ void band_attn_kernel(Params prm) {
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
           for (int db = 0; db < kOT; ++db) {
-            const SSW_LDS char* vp = vbase + v_off[db] + 16 * t * Lay::kRowBytes;
+            const SSW_LDS char* vp =
+                vbase + (kLean ? (opaque(v_off[0]) ^ (db << 6)) : v_off[db]) + 16 * t * Lay::kRowBytes;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SSW_LDS s16x4*)vp);
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (SSW_LDS s16x4*)(vp + 4 * Lay::kRowBytes));
@@ -1212,14 +1325,14 @@ __global__ void neighbor_mask_kernel(const int32_t* sigma, int n, int L, int R, 
 }
 
 // ---- host-side dispatch
-template <typename T, int D, bool PERM, bool SIGMASK, int EPI>
+template <typename T, int D, bool PERM, bool SIGMASK, int EPI, bool W3 = false>
 static hipError_t launch_t(const Params& prm, hipStream_t stream, void* ev_start, void* ev_stop) {
   if (ev_start || ev_stop) {
-    hipExtLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, EPI>), dim3(prm.nblocks),
+    hipExtLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, EPI, W3>), dim3(prm.nblocks),
                           dim3(kThreads), 0, stream, (hipEvent_t)ev_start, (hipEvent_t)ev_stop, 0,
                           prm);
   } else {
-    hipLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, EPI>), dim3(prm.nblocks),
+    hipLaunchKernelGGL((band_attn_kernel<T, D, PERM, SIGMASK, EPI, W3>), dim3(prm.nblocks),
                        dim3(kThreads), 0, stream, prm);
   }
   return hipGetLastError();
@@ -1232,11 +1345,18 @@ static hipError_t launch_d(const BandLaunch& a, const Params& prm, hipStream_t s
   // The SA pass of the gated path adds to the SWA pass's intermediate; nothing else combines.
   if (a.perm) {
     const bool add = a.epilogue == kEpiAddPartial;
-    if (a.causal)
-      return add ? launch_t<T, D, true, true, kEpiAddPartial>(prm, s, e0, e1)
-                 : launch_t<T, D, true, true, kEpiStore>(prm, s, e0, e1);
-    return add ? launch_t<T, D, true, false, kEpiAddPartial>(prm, s, e0, e1)
-               : launch_t<T, D, true, false, kEpiStore>(prm, s, e0, e1);
+    // SA alone (bf16): the three-waves-per-SIMD build when a workgroup's band, at most
+    // ceil(kColsWG / G) + 1 slots plus L + R keys, fits its 1024-entry sigma segment
+    const int64_t band = (kColsWG + prm.G - 1) / prm.G + 1 + (int64_t)prm.L + prm.R;
+    const bool w3 = SSW_W3_STORE && sizeof(T) == 2 && !add && band <= SSW_SIGCAP_W3;
+    if (a.causal) {
+      if (add) return launch_t<T, D, true, true, kEpiAddPartial>(prm, s, e0, e1);
+      return w3 ? launch_t<T, D, true, true, kEpiStore, true>(prm, s, e0, e1)
+                : launch_t<T, D, true, true, kEpiStore>(prm, s, e0, e1);
+    }
+    if (add) return launch_t<T, D, true, false, kEpiAddPartial>(prm, s, e0, e1);
+    return w3 ? launch_t<T, D, true, false, kEpiStore, true>(prm, s, e0, e1)
+              : launch_t<T, D, true, false, kEpiStore>(prm, s, e0, e1);
   }
   return a.epilogue == kEpiPartial ? launch_t<T, D, false, false, kEpiPartial>(prm, s, e0, e1)
                                    : launch_t<T, D, false, false, kEpiStore>(prm, s, e0, e1);
