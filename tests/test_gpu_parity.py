@@ -340,3 +340,25 @@ def test_full_size_workloads_sampled_rows(index):
                 err = _maxerr(got, ref, wl.dtype)
                 _say(f"   max err {err:.3e}")
                 assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("w", [496, 497])
+@pytest.mark.parametrize("causal", [True, False])
+def test_sa_alone_build_switch(w, causal):
+    """SA alone has two builds: three waves per SIMD when a workgroup's band (ceil(128 / G) + 1
+    slots plus 2(w - 1) keys) fits its 1024-entry sigma segment, two waves otherwise.  At G = 4
+    the switch lies between w = 496 and w = 497; both sides against the oracle on sampled rows
+    (first, last, tile boundaries, random), bf16 bar."""
+    B, n, Hq, Hkv, d = 1, 2048, 8, 2, 128
+    host, dev = _data(41, B, n, Hq, Hkv, d, "bf16")
+    sig_dev, sig = _sigma(42, n)
+    q, k, v, _ = dev
+    out = ssw.sa_forward(q, k, v, sig_dev, w, causal)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(43)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 33, n - 2, n - 1],
+                                     rng.choice(n, size=40, replace=False)]))
+    qh, kh, vh, _ = host
+    ref = oracle.sa_rows(qh, kh, vh, sig, w, causal, rows)
+    err = _maxerr(out[:, rows], ref, "bf16")
+    _say(f"SA alone w={w} causal={causal}: max err {err:.3e}")
