@@ -284,7 +284,7 @@ __device__ __forceinline__ int xcd_local_order(int i, int nblocks) {
 }
 
 template <typename T, bool PERM, int EPI, bool W3>
-constexpr bool kIsW3 = W3 && PERM && sizeof(T) == 2 && EPI == kEpiStore;
+constexpr bool kIsW3 = W3 && PERM && sizeof(T) == 2 && EPI != kEpiPartial;
 template <typename T, bool PERM, int EPI, bool W3>
 constexpr int kWavesPerEU =
     kIsW3<T, PERM, EPI, W3> ? 3 : (PERM || sizeof(T) != 2) ? SSW_WPE : SSW_WPE_SWA;
@@ -303,7 +303,7 @@ void band_attn_kernel(Params prm) {
   // lane constants at their use instead of holding them across the loop: the DMA row keys and
   // offsets, the K/V LDS offsets (one base register each), and it reads sigma for the causal
   // mask in two halves.
-  constexpr bool kLeanAny = kW3 && SIGMASK;
+  constexpr bool kLeanAny = kW3 && SIGMASK && D == 128;
 #ifndef SSW_LEAN_DMA
 #define SSW_LEAN_DMA 1
 #endif
@@ -1345,16 +1345,26 @@ static hipError_t launch_d(const BandLaunch& a, const Params& prm, hipStream_t s
   // The SA pass of the gated path adds to the SWA pass's intermediate; nothing else combines.
   if (a.perm) {
     const bool add = a.epilogue == kEpiAddPartial;
-    // SA alone (bf16): the three-waves-per-SIMD build when a workgroup's band, at most
-    // ceil(kColsWG / G) + 1 slots plus L + R keys, fits its 1024-entry sigma segment
+    // The three-waves-per-SIMD build when a workgroup's band, at most ceil(kColsWG / G) + 1 slots
+    // plus L + R keys, fits its 1024-entry sigma segment: SA alone (bf16), and the gated layer's
+    // SA pass at d = 64 (at d = 128 that pass does not fit 168 registers).
     const int64_t band = (kColsWG + prm.G - 1) / prm.G + 1 + (int64_t)prm.L + prm.R;
     const bool w3 = SSW_W3_STORE && sizeof(T) == 2 && !add && band <= SSW_SIGCAP_W3;
+    const bool w3g = SSW_W3_STORE && sizeof(T) == 2 && band <= SSW_SIGCAP_W3;
     if (a.causal) {
-      if (add) return launch_t<T, D, true, true, kEpiAddPartial>(prm, s, e0, e1);
+      if (add) {
+        if constexpr (D == 64)
+          if (w3g) return launch_t<T, D, true, true, kEpiAddPartial, true>(prm, s, e0, e1);
+        return launch_t<T, D, true, true, kEpiAddPartial>(prm, s, e0, e1);
+      }
       return w3 ? launch_t<T, D, true, true, kEpiStore, true>(prm, s, e0, e1)
                 : launch_t<T, D, true, true, kEpiStore>(prm, s, e0, e1);
     }
-    if (add) return launch_t<T, D, true, false, kEpiAddPartial>(prm, s, e0, e1);
+    if (add) {
+      if constexpr (D == 64)
+        if (w3g) return launch_t<T, D, true, false, kEpiAddPartial, true>(prm, s, e0, e1);
+      return launch_t<T, D, true, false, kEpiAddPartial>(prm, s, e0, e1);
+    }
     return w3 ? launch_t<T, D, true, false, kEpiStore, true>(prm, s, e0, e1)
               : launch_t<T, D, true, false, kEpiStore>(prm, s, e0, e1);
   }
