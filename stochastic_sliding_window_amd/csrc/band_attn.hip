@@ -31,6 +31,10 @@
 //     Masks are evaluated per element only where a chunk touches the band edge or when the causal
 //     rule needs sigma.
 //   * Epilogue: divide by the row sum, multiply by the gate, scatter to row sigma[p].
+//   * Two builds (template flag W3): two waves per SIMD with a 4-slot ring and two chunks per
+//     loop step, and, for SA alone and the d = 64 gated SA pass, three waves per SIMD with a
+//     3-slot ring and one chunk per step; the dispatcher picks the latter when a workgroup's band
+//     fits its sigma segment.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -103,6 +107,16 @@ constexpr int kStages = SSW_STAGES;  // LDS ring depth: kStages - 1 chunks in fl
 #endif
 #ifndef SSW_SIGCAP_W3
 #define SSW_SIGCAP_W3 1024
+#endif
+// parts of the register diet of the three-waves causal build at d = 128 (tuning switches)
+#ifndef SSW_LEAN_DMA
+#define SSW_LEAN_DMA 1
+#endif
+#ifndef SSW_LEAN_KV
+#define SSW_LEAN_KV 1
+#endif
+#ifndef SSW_LEAN_MASK
+#define SSW_LEAN_MASK 1
 #endif
 constexpr int kSigCap = SSW_SIGCAP;  // sigma entries held in LDS at a time
 constexpr float kLazy = 8.0f;  // reference max may lag the true max by up to 2^8 (log2 units)
@@ -299,20 +313,11 @@ void band_attn_kernel(Params prm) {
   constexpr int kSegChunks = Lay::kSegChunks;  // chunks per sigma segment
   constexpr bool kPipe = kW3 ? false : PERM ? SSW_PIPELINE : SSW_PIPELINE_SWA;
   constexpr bool kBf16 = Lay::kBf16;
-  // At three waves per SIMD (168 registers) the causal sigma-gathered kernel recomputes some
-  // lane constants at their use instead of holding them across the loop: the DMA row keys and
-  // offsets, the K/V LDS offsets (one base register each), and it reads sigma for the causal
-  // mask in two halves.
+  // At three waves per SIMD (168 registers) the causal sigma-gathered kernel at d = 128
+  // recomputes some lane constants at their use instead of holding them across the loop: the
+  // DMA row keys and offsets, the K/V LDS offsets (one base register each), and it reads sigma
+  // for the causal mask in two halves.  (d = 64 fits without.)
   constexpr bool kLeanAny = kW3 && SIGMASK && D == 128;
-#ifndef SSW_LEAN_DMA
-#define SSW_LEAN_DMA 1
-#endif
-#ifndef SSW_LEAN_KV
-#define SSW_LEAN_KV 1
-#endif
-#ifndef SSW_LEAN_MASK
-#define SSW_LEAN_MASK 1
-#endif
   constexpr bool kLeanDma = kLeanAny && SSW_LEAN_DMA;
   constexpr bool kLean = kLeanAny && SSW_LEAN_KV;  // K/V LDS offsets
   constexpr bool kLeanMask = kLeanAny && SSW_LEAN_MASK;
