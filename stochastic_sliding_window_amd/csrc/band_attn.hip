@@ -108,9 +108,12 @@ constexpr int kStages = SSW_STAGES;  // LDS ring depth: kStages - 1 chunks in fl
 #ifndef SSW_SIGCAP_W3
 #define SSW_SIGCAP_W3 1024
 #endif
-// parts of the register diet of the three-waves causal build at d = 128 (tuning switches)
+// parts of the register diet of the three-waves causal build at d = 128 (tuning switches).
+// Recomputing the DMA row keys and offsets at each issue fits the last register without a spill
+// but costs more than the one spill outside the loop it avoids (about 8% on causal SA alone),
+// so it is off.
 #ifndef SSW_LEAN_DMA
-#define SSW_LEAN_DMA 1
+#define SSW_LEAN_DMA 0
 #endif
 #ifndef SSW_LEAN_KV
 #define SSW_LEAN_KV 1
@@ -314,9 +317,9 @@ void band_attn_kernel(Params prm) {
   constexpr bool kPipe = kW3 ? false : PERM ? SSW_PIPELINE : SSW_PIPELINE_SWA;
   constexpr bool kBf16 = Lay::kBf16;
   // At three waves per SIMD (168 registers) the causal sigma-gathered kernel at d = 128
-  // recomputes some lane constants at their use instead of holding them across the loop: the
-  // DMA row keys and offsets, the K/V LDS offsets (one base register each), and it reads sigma
-  // for the causal mask in two halves.  (d = 64 fits without.)
+  // recomputes the K/V LDS offsets at their use (from one base register each) instead of holding
+  // them across the loop, and reads sigma for the causal mask in two halves.  (d = 64 fits
+  // without.)
   constexpr bool kLeanAny = kW3 && SIGMASK && D == 128;
   constexpr bool kLeanDma = kLeanAny && SSW_LEAN_DMA;
   constexpr bool kLean = kLeanAny && SSW_LEAN_KV;  // K/V LDS offsets
