@@ -362,3 +362,24 @@ def test_sa_alone_build_switch(w, causal):
     ref = oracle.sa_rows(qh, kh, vh, sig, w, causal, rows)
     err = _maxerr(out[:, rows], ref, "bf16")
     _say(f"SA alone w={w} causal={causal}: max err {err:.3e}")
+
+
+@pytest.mark.parametrize("w", [448, 449])
+def test_gated_d64_build_switch(w):
+    """The gated layer's SA pass at d = 64 also has a three-waves-per-SIMD build, used when a
+    workgroup's band fits its 1024-entry sigma segment; with one query head per KV head (G = 1)
+    the switch lies between w = 448 and w = 449.  Both sides of the gated layer against the oracle
+    on sampled rows, bf16 bar."""
+    B, n, Hq, Hkv, d = 2, 1536, 2, 2, 64
+    host, dev = _data(51, B, n, Hq, Hkv, d, "bf16")
+    sig_dev, sig = _sigma(52, n)
+    q, k, v, g = dev
+    out = ssw.gated_sa_swa_forward(q, k, v, sig_dev, w, True, g)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(53)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, n - 2, n - 1],
+                                     rng.choice(n, size=40, replace=False)]))
+    qh, kh, vh, gh = host
+    ref = oracle.gated_forward(qh, kh, vh, sig, w, True, gh, rows)
+    err = _maxerr(out[:, rows], ref, "bf16")
+    _say(f"gated d64 w={w}: max err {err:.3e}")
