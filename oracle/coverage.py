@@ -12,8 +12,17 @@ The coverage after l layers is sum_i |R_l(i)| divided by the number of pairs (su
 causal, n^2 otherwise): the share of pairs whose information has reached i.  Plain Python sets,
 for small n only.
 
-Pins (tests/test_coverage.py): SWA has closed forms: causal R_l(i) = [max(0, i - l (w - 1)), i],
-non-causal the interval |i - j| <= l (w - 1) cut to [0, n).
+Pins (tests/test_coverage.py), none of which calls this function's helpers:
+  * SWA closed forms: causal R_l(i) = [max(0, i - l (w - 1)), i], non-causal the interval
+    |i - j| <= l (w - 1) cut to [0, n);
+  * one SA layer: exactly n w - w (w - 1) / 2 attended pairs when causal (each unordered
+    in-band pair points back in original order one way, whatever sigma is) and
+    n (2 w - 1) - w (w - 1) when not;
+  * a window spanning the sequence covers everything after one layer, a unit window never grows;
+  * every mode over four layers equals a second formulation: boolean products of dense
+    adjacency matrices built from the slot-space band itself;
+  * planted mistakes (one sigma for all layers, an intersection for the gated layer, an
+    in-place update, a wrong start, a wrong pair total) each fail one of these.
 """
 
 from __future__ import annotations
