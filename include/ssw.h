@@ -86,19 +86,20 @@ int ssw_swa_forward(const void* q, const void* k, const void* v, const int32_t* 
 /* Gated dual path ([SA-ja] ゲート付き SA と SWA の組み合わせ):
  *   out = g_sa (.) SA(q, k, v; sigma, w, causal) + g_swa (.) SWA(q, k, v; w, causal).
  *   gates     device float32 [2, B, n, Hq], required.  Both paths use the same w and causal.
- * Two kernels run back to back on `stream`: the SWA pass leaves g_swa (.) Y_swa in `out` as an
- * intermediate, then the SA pass reads it at each scattered row, adds g_sa (.) Y_sa and stores the
- * sum.  For fp32 the intermediate is fp32.  For bf16 it is held, in the same two bytes per
- * element, as fp16 bits of g_swa (.) Y_swa * 2^-8 (8x finer than bf16), so the result is in effect
- * rounded to bf16 once; this needs |g_swa (.) Y_swa| < 1.6e7 (true whenever |V| < 1.6e7).
- * Between the two passes `out` holds that intermediate, not a result.  Other arguments as in
- * ssw_sa_forward. */
+ * Two kernels run back to back on `stream`: the SA pass leaves g_sa (.) Y_sa in `out` as an
+ * intermediate, at the scattered rows sigma[p], then the SWA pass reads it at its own rows, adds
+ * g_swa (.) Y_swa and stores the sum.  For fp32 the intermediate is fp32.  For bf16 it is held,
+ * in the same two bytes per element, as fp16 bits of g_sa (.) Y_sa * 2^-8, so the result is in
+ * effect rounded to bf16 once: for |g_sa (.) Y_sa| >= 2^-6 that keeps 3 more significand bits
+ * than bf16, below it the step is a fixed 2^-16 (absolute error <= 2^-17 = 7.6e-6); it needs
+ * |g_sa (.) Y_sa| < 1.6e7 (true whenever |V| < 1.6e7).  Between the two passes `out` holds that
+ * intermediate, not a result.  Other arguments as in ssw_sa_forward. */
 int ssw_gated_sa_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma,
                              int window, int causal, const float* gates, void* out,
                              int B, int n, int Hq, int Hkv, int d, int dtype, void* stream);
 
-/* Same as ssw_gated_sa_swa_forward, and additionally times each of its two kernels: the given
- * HIP events (hipEvent_t created by the caller; each may be NULL) are attached to the kernels'
+/* Same as ssw_gated_sa_swa_forward, and additionally times each of its two kernels (the SA
+ * pass runs first): the given HIP events (hipEvent_t created by the caller; each may be NULL) are attached to the kernels'
  * dispatches, so ev_swa_start / ev_swa_end are recorded when the SWA pass starts and ends and
  * ev_sa_start / ev_sa_end likewise for the SA pass.  No separate event packets are queued, so the
  * calls run back to back as in the untimed form and hipEventElapsedTime gives each kernel's own

@@ -301,7 +301,7 @@ __device__ __forceinline__ int xcd_local_order(int i, int nblocks) {
 }
 
 template <typename T, bool PERM, int EPI, bool W3>
-constexpr bool kIsW3 = W3 && PERM && sizeof(T) == 2 && EPI != kEpiPartial;
+constexpr bool kIsW3 = W3 && PERM && sizeof(T) == 2;
 template <typename T, bool PERM, int EPI, bool W3>
 constexpr int kWavesPerEU =
     kIsW3<T, PERM, EPI, W3> ? 3 : (PERM || sizeof(T) != 2) ? SSW_WPE : SSW_WPE_SWA;
@@ -517,11 +517,17 @@ void band_attn_kernel(Params prm) {
 
   const int64_t qrow_elems = (((int64_t)b * n + myorig) * prm.Hq + h) * D;
   // the gate is fetched now, with Q, instead of in the epilogue
-  const float gate_v = prm.gate ? prm.gate[((int64_t)b * n + myorig) * prm.Hq + h] : 1.0f;
+  // A malformed sigma (an entry outside [0, n); sigma is trusted unless the caller asks for
+  // validation) must not turn into a memory fault: such a column reads no gate or Q row and
+  // stores nothing.  Its K/V row loads need no test, since buffer loads past the range read
+  // zeros.
+  const bool rowvalid = colvalid && (uint32_t)myorig < (uint32_t)n;
+  const float gate_v =
+      prm.gate && rowvalid ? prm.gate[((int64_t)b * n + myorig) * prm.Hq + h] : 1.0f;
   // byte offset of this column's output row within batch row b (the out buffer holds
   // n * Hq * D elements per batch row, < 2^31 bytes as checked at the API)
   const uint32_t out_off =
-      colvalid ? (uint32_t)(((int64_t)myorig * prm.Hq + h) * (D * (int)sizeof(T))) : kOutOfRange;
+      rowvalid ? (uint32_t)(((int64_t)myorig * prm.Hq + h) * (D * (int)sizeof(T))) : kOutOfRange;
   constexpr int kQRegs = kBf16 ? D / 16 : D / 2;
   typedef typename std::conditional<kBf16, bf16x8, float>::type QFrag;
   QFrag qf[kQRegs];
@@ -549,14 +555,14 @@ void band_attn_kernel(Params prm) {
     const char* qp = prm.q + (qrow_elems + 8 * h32) * 2;
 #pragma unroll
     for (int kb = 0; kb < kQRegs; ++kb) {
-      u32x4 raw = colvalid ? *(const u32x4*)(qp + kb * 32) : u32x4{0, 0, 0, 0};
+      u32x4 raw = rowvalid ? *(const u32x4*)(qp + kb * 32) : u32x4{0, 0, 0, 0};
       qf[kb] = __builtin_bit_cast(bf16x8, raw);
     }
   } else {
     const char* qp = prm.q + (qrow_elems + h32 * (D / 2)) * 4;
 #pragma unroll
     for (int t4 = 0; t4 < D / 8; ++t4) {
-      f32x4 v4 = colvalid ? *(const f32x4*)(qp + t4 * 16) : f32x4{0, 0, 0, 0};
+      f32x4 v4 = rowvalid ? *(const f32x4*)(qp + t4 * 16) : f32x4{0, 0, 0, 0};
       qf[4 * t4 + 0] = v4[0];
       qf[4 * t4 + 1] = v4[1];
       qf[4 * t4 + 2] = v4[2];
@@ -1216,7 +1222,7 @@ void band_attn_kernel(Params prm) {
   if (!wave_on) return;
   // The row's log-sum-exp for a backward pass.  Every row holds its own token, so m_ref is finite
   // and l_tot >= 1 here; l_tot sums exp2 of the scaled scores minus m_ref.
-  if (prm.lse && h32 == 0 && colvalid)
+  if (prm.lse && h32 == 0 && rowvalid)
     prm.lse[((int64_t)b * n + myorig) * prm.Hq + h] =
         (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   const float f = __builtin_amdgcn_rcpf(l_tot) * gate_v;
@@ -1254,7 +1260,7 @@ void band_attn_kernel(Params prm) {
         } else {
           if constexpr (EPI == kEpiAddPartial) {
             const u32x2 old = kPrefetchPartial ? *slot : *(const u32x2*)(prm.out +
-                                  (int64_t)b * out_batch_bytes + (colvalid ? out_off : 0u) +
+                                  (int64_t)b * out_batch_bytes + (rowvalid ? out_off : 0u) +
                                   d0 * 2);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -1290,7 +1296,7 @@ void band_attn_kernel(Params prm) {
       if (roff != kOutOfRange) *(u32x4*)(obatch + roff + 16 * gran) = v;
     }
   } else {
-    if (!colvalid) return;
+    if (!rowvalid) return;
     char* orow = prm.out + qrow_elems * (int64_t)sizeof(T);
 #pragma unroll
     for (int t = 0; t < kOT; ++t) {
@@ -1350,34 +1356,31 @@ template <typename T, int D>
 static hipError_t launch_d(const BandLaunch& a, const Params& prm, hipStream_t s) {
   void* e0 = a.ev_start;
   void* e1 = a.ev_stop;
-  // The SA pass of the gated path adds to the SWA pass's intermediate; nothing else combines.
+  // The gated layer runs its SA pass first, which leaves the intermediate (kEpiPartial), and its
+  // SWA pass second, which adds to it (kEpiAddPartial); everything else stores plainly.
   if (a.perm) {
-    const bool add = a.epilogue == kEpiAddPartial;
-    // The three-waves-per-SIMD build when a workgroup's band, at most ceil(kColsWG / G) + 1 slots
-    // plus L + R keys, fits its 1024-entry sigma segment: SA alone (bf16), and the gated layer's
-    // SA pass at d = 64 (at d = 128 that pass does not fit 168 registers).
+    const bool part = a.epilogue == kEpiPartial;
+    // The three-waves-per-SIMD build (bf16) when a workgroup's band, at most ceil(kColsWG / G)
+    // + 1 slots plus L + R keys, fits its 1024-entry sigma segment.
     const int64_t band = (kColsWG + prm.G - 1) / prm.G + 1 + (int64_t)prm.L + prm.R;
-    const bool w3 = SSW_W3_STORE && sizeof(T) == 2 && !add && band <= SSW_SIGCAP_W3;
-    const bool w3g = SSW_W3_STORE && sizeof(T) == 2 && band <= SSW_SIGCAP_W3;
-    if (a.causal) {
-      if (add) {
-        if constexpr (D == 64)
-          if (w3g) return launch_t<T, D, true, true, kEpiAddPartial, true>(prm, s, e0, e1);
-        return launch_t<T, D, true, true, kEpiAddPartial>(prm, s, e0, e1);
+    if constexpr (sizeof(T) == 2) {
+      if (SSW_W3_STORE && band <= SSW_SIGCAP_W3) {
+        if (a.causal)
+          return part ? launch_t<T, D, true, true, kEpiPartial, true>(prm, s, e0, e1)
+                      : launch_t<T, D, true, true, kEpiStore, true>(prm, s, e0, e1);
+        return part ? launch_t<T, D, true, false, kEpiPartial, true>(prm, s, e0, e1)
+                    : launch_t<T, D, true, false, kEpiStore, true>(prm, s, e0, e1);
       }
-      return w3 ? launch_t<T, D, true, true, kEpiStore, true>(prm, s, e0, e1)
-                : launch_t<T, D, true, true, kEpiStore>(prm, s, e0, e1);
     }
-    if (add) {
-      if constexpr (D == 64)
-        if (w3g) return launch_t<T, D, true, false, kEpiAddPartial, true>(prm, s, e0, e1);
-      return launch_t<T, D, true, false, kEpiAddPartial>(prm, s, e0, e1);
-    }
-    return w3 ? launch_t<T, D, true, false, kEpiStore, true>(prm, s, e0, e1)
-              : launch_t<T, D, true, false, kEpiStore>(prm, s, e0, e1);
+    if (a.causal)
+      return part ? launch_t<T, D, true, true, kEpiPartial>(prm, s, e0, e1)
+                  : launch_t<T, D, true, true, kEpiStore>(prm, s, e0, e1);
+    return part ? launch_t<T, D, true, false, kEpiPartial>(prm, s, e0, e1)
+                : launch_t<T, D, true, false, kEpiStore>(prm, s, e0, e1);
   }
-  return a.epilogue == kEpiPartial ? launch_t<T, D, false, false, kEpiPartial>(prm, s, e0, e1)
-                                   : launch_t<T, D, false, false, kEpiStore>(prm, s, e0, e1);
+  return a.epilogue == kEpiAddPartial
+             ? launch_t<T, D, false, false, kEpiAddPartial>(prm, s, e0, e1)
+             : launch_t<T, D, false, false, kEpiStore>(prm, s, e0, e1);
 }
 
 hipError_t launch_band_attn(const BandLaunch& a, hipStream_t stream) {

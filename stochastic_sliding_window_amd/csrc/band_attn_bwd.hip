@@ -53,6 +53,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 // chunk's row loads wait for one memory latency instead of two (sigma, then the row)
 constexpr int kSigCap = 2048;
 
+// An entry of a malformed sigma (sigma is trusted unless the caller asks for validation) is
+// taken as token 0: the result is wrong, but every row it selects lies inside the tensors, so it
+// cannot become a memory fault.
+__device__ __forceinline__ int in_range(int tok, int n) {
+  return (uint32_t)tok < (uint32_t)n ? tok : 0;
+}
+
 struct Params {
   const char* q;
   const char* k;
@@ -264,7 +271,7 @@ void bwd_dq_kernel(Params prm) {
   const int mycol_c = colvalid ? mycol : nG - 1;
   const int myslot = mycol_c / G;
   const int h = g * G + (mycol_c - myslot * G);
-  const int myorig = PERM ? prm.sigma[myslot] : myslot;
+  const int myorig = PERM ? in_range(prm.sigma[myslot], n) : myslot;
   const bool wave_on = col0_w < nG;
   const int w_slo = min(col0_w, nG - 1) / G;
   const int w_shi = min(col0_w + 31, nG - 1) / G;
@@ -313,7 +320,7 @@ void bwd_dq_kernel(Params prm) {
   auto load_sigma_seg = [&]() {
     for (int i = tid; i < kSigCap; i += kThreads) {
       const int key = seg_key0 + i;
-      sig_lds[i] = key < n ? prm.sigma[key] : INT_MAX;
+      sig_lds[i] = key < n ? in_range(prm.sigma[key], n) : INT_MAX;
     }
   };
 
@@ -495,7 +502,7 @@ void bwd_dkdv_kernel(Params prm) {
   const int myk = kw0 + r32;
   const bool keyvalid = myk < n;
   const int myk_c = keyvalid ? myk : n - 1;
-  const int ktok = PERM ? prm.sigma[myk_c] : myk_c;
+  const int ktok = PERM ? in_range(prm.sigma[myk_c], n) : myk_c;
   const bool wave_on = kw0 < n;
   // key q is in the band of the query slots [q - R, q + L]
   const int khi_wg = min(K0 + kTile - 1, n - 1);
@@ -525,7 +532,7 @@ void bwd_dkdv_kernel(Params prm) {
   auto load_sigma_seg = [&](int s0) {
     for (int i = tid; i < kSigCap; i += kThreads) {
       const int slot = s0 + i;
-      sig_lds[i] = slot < n ? prm.sigma[slot] : 0;
+      sig_lds[i] = slot < n ? in_range(prm.sigma[slot], n) : 0;
     }
   };
   auto orig_of_slot = [&](int slot) { return PERM ? sig_lds[slot - seg_s0] : slot; };

@@ -110,7 +110,9 @@ void decode_kernel(Params prm) {
   // ---- the candidate chunks of both paths as one sequence: SA slots [p - L, p + L] first
   // (chunks [0, nA)), then SWA positions [t - L, t] (chunks [nA, nA + nB))
   const bool do_sa = prm.paths & 1;
-  const int p_sa = do_sa ? prm.inv[tc] : 0;
+  // (an entry of a malformed inverse outside [0, n) is taken as slot 0: wrong, but in bounds)
+  const int p_raw = do_sa ? prm.inv[tc] : 0;
+  const int p_sa = (uint32_t)p_raw < (uint32_t)n ? p_raw : 0;
   const int lo_sa = max(0, p_sa - L);
   const int hi_sa = min(n - 1, p_sa + L);
   const int nA = do_sa ? (hi_sa - lo_sa) / kCand + 1 : 0;
@@ -124,7 +126,8 @@ void decode_kernel(Params prm) {
       const int q = lo_sa + c * kCand + j;
       ok = q <= hi_sa;
       tok = ok ? prm.sigma[q] : tc;
-      ok = ok && tok <= tc;
+      // unsigned: an entry of a malformed sigma below 0 is masked too, and never read
+      ok = ok && (uint32_t)tok <= (uint32_t)tc;
     } else {
       const int q = lo_w + (c - nA) * kCand + j;
       ok = q <= tc;

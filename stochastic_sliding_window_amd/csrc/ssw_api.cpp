@@ -160,6 +160,42 @@ int ssw_swa_forward(const void* q, const void* k, const void* v, const int32_t* 
              (hipStream_t)stream);
 }
 
+// The gated layer's two passes (arguments already checked): the SA pass (sigma of batch row b
+// and KV head g at sigma + b * sb + g * sh) leaves the intermediate, the SWA pass adds to it.
+static int run_gated(const char* who, const void* q, const void* k, const void* v,
+                     const int32_t* sigma, int64_t sb, int64_t sh, int window, int causal,
+                     const float* gates, void* out, int B, int n, int Hq, int Hkv, int d,
+                     int dtype, hipStream_t s, void* const* events) {
+  const float* g_sa = gates;
+  const float* g_swa = gates + (size_t)B * n * Hq;
+  // Pass 1: the SA pass leaves g_sa * Y_sa in `out` as the intermediate, at the scattered rows
+  // sigma[p] (fp32, or for bf16 outputs fp16 bits of the value times 2^-8, so that the sum is
+  // in effect rounded to bf16 once).  sigma being a bijection means every row is written once.
+  ssw::BandLaunch a1 =
+      make_launch(q, k, v, sigma, window, causal, g_sa, out, B, n, Hq, Hkv, d, dtype);
+  a1.epilogue = ssw::kEpiPartial;
+  a1.sig_bstride = sb;
+  a1.sig_hstride = sh;
+  // Pass 2: the SWA pass reads the intermediate of its own (contiguous) rows, adds
+  // g_swa * Y_swa and stores the result.  Stream order makes the read-modify-write race-free.
+  // This order keeps the read-modify-write out of the sigma-gathered pass, which has the more
+  // arithmetic per byte of the two.
+  ssw::BandLaunch a2 =
+      make_launch(q, k, v, nullptr, window, causal, g_swa, out, B, n, Hq, Hkv, d, dtype);
+  a2.epilogue = ssw::kEpiAddPartial;
+  if (events) {
+    // events[0..1] bracket the SWA pass and events[2..3] the SA pass, whatever their order
+    a2.ev_start = events[0];
+    a2.ev_stop = events[1];
+    a1.ev_start = events[2];
+    a1.ev_stop = events[3];
+  }
+  int st = run(who, a1, s);
+  if (st != SSW_OK) return st;
+  return run(who, a2, s);
+}
+
+
 static int gated(const char* who, const void* q, const void* k, const void* v,
                  const int32_t* sigma, int window, int causal, const float* gates, void* out,
                  int B, int n, int Hq, int Hkv, int d, int dtype, void* stream,
@@ -174,27 +210,8 @@ static int gated(const char* who, const void* q, const void* k, const void* v,
     st = check_sigma_on_device(sigma, n, s);
     if (st != SSW_OK) return st;
   }
-  const float* g_sa = gates;
-  const float* g_swa = gates + (size_t)B * n * Hq;
-  // Pass 1: the SWA pass leaves g_swa * Y_swa in `out` as the intermediate (fp32, or for bf16
-  // outputs fp16 bits of the value times 2^-8, so that the sum is in effect rounded to bf16 once).
-  ssw::BandLaunch a1 =
-      make_launch(q, k, v, nullptr, window, causal, g_swa, out, B, n, Hq, Hkv, d, dtype);
-  a1.epilogue = ssw::kEpiPartial;
-  // Pass 2: the SA pass reads the intermediate at each scattered row sigma[p], adds
-  // g_sa * Y_sa and stores the result.  Stream order makes the read-modify-write race-free and
-  // sigma being a bijection means no two lanes touch the same row.
-  ssw::BandLaunch a2 =
-      make_launch(q, k, v, sigma, window, causal, g_sa, out, B, n, Hq, Hkv, d, dtype);
-  a2.epilogue = ssw::kEpiAddPartial;
-  if (events) {
-    a1.ev_start = events[0];
-    a1.ev_stop = events[1];
-    a2.ev_start = events[2];
-    a2.ev_stop = events[3];
-  }
-  if ((st = run(who, a1, s)) != SSW_OK) return st;
-  return run(who, a2, s);
+  return run_gated(who, q, k, v, sigma, 0, 0, window, causal, gates, out, B, n, Hq, Hkv, d,
+                   dtype, s, events);
 }
 
 int ssw_gated_sa_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma,
@@ -250,16 +267,8 @@ static int forward_ex(const char* who, const void* q, const void* k, const void*
     a.sig_hstride = sh;
     return run(who, a, s);
   }
-  ssw::BandLaunch a1 = make_launch(q, k, v, nullptr, window, causal, gates + (size_t)B * n * Hq,
-                                   out, B, n, Hq, Hkv, d, dtype);
-  a1.epilogue = ssw::kEpiPartial;
-  ssw::BandLaunch a2 =
-      make_launch(q, k, v, sigma, window, causal, gates, out, B, n, Hq, Hkv, d, dtype);
-  a2.epilogue = ssw::kEpiAddPartial;
-  a2.sig_bstride = sb;
-  a2.sig_hstride = sh;
-  if ((st = run(who, a1, s)) != SSW_OK) return st;
-  return run(who, a2, s);
+  return run_gated(who, q, k, v, sigma, sb, sh, window, causal, gates, out, B, n, Hq, Hkv, d,
+                   dtype, s, nullptr);
 }
 
 int ssw_sa_forward_ex(const void* q, const void* k, const void* v, const int32_t* sigma,

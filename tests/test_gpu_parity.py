@@ -226,9 +226,10 @@ def test_timed_gated_call_matches_untimed():
     b = ssw.gated_sa_swa_forward(q, k, v, sig_dev, w, True, g, events=evs)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
-    # each pair brackets one kernel; the SA pass starts no earlier than the SWA pass ends
+    # each pair brackets one kernel (0, 1: the SWA pass; 2, 3: the SA pass); the SA pass runs
+    # first, and the SWA pass starts no earlier than it ends
     assert evs[0].elapsed_time(evs[1]) > 0 and evs[2].elapsed_time(evs[3]) > 0
-    assert evs[1].elapsed_time(evs[2]) >= 0
+    assert evs[3].elapsed_time(evs[0]) >= 0
 
 
 def test_empty_inputs_are_noops():
