@@ -30,11 +30,12 @@
 //     by more than 2^8); the row sum is taken over the bf16-rounded weights the P*V product uses.
 //     Masks are evaluated per element only where a chunk touches the band edge or when the causal
 //     rule needs sigma.
-//   * Epilogue: divide by the row sum, multiply by the gate, scatter to row sigma[p].
-//   * Two builds (template flag W3): two waves per SIMD with a 4-slot ring and two chunks per
-//     loop step, and, for SA alone and the d = 64 gated SA pass, three waves per SIMD with a
-//     3-slot ring and one chunk per step; the dispatcher picks the latter when a workgroup's band
-//     fits its sigma segment.
+//   * Epilogue: divide by the row sum, multiply by the gate, scatter to row sigma[p] (the gated
+//     layer's SA pass stores its fp16 intermediate there; its SWA pass adds to it).
+//   * Two builds of the sigma-gathered kernel (template flag W3): two waves per SIMD with a
+//     4-slot ring and two chunks per loop step, and (bf16) three waves per SIMD with a 3-slot
+//     ring and one chunk per step; the dispatcher picks the latter when a workgroup's band fits
+//     its sigma segment.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -48,6 +49,9 @@ namespace ssw {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -56,74 +60,32 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define SSW_LDS __attribute__((address_space(3)))
 
-#ifndef SSW_WAVES
-#define SSW_WAVES 4
-#endif
-#ifndef SSW_STAGES
-#define SSW_STAGES 4
-#endif
-#ifndef SSW_WPE
-#define SSW_WPE 2  // waves per SIMD the register allocation is sized for
-#endif
-#ifndef SSW_STEP2
-#define SSW_STEP2 1  // bf16: two 32-key chunks per loop step
-#endif
-#ifndef SSW_PIPELINE
-#define SSW_PIPELINE 1  // scores of chunk c + 1 computed alongside the softmax of chunk c
-#endif
-// The identity-sigma (SWA) kernels hold no sigma in LDS and fewer registers without the score
-// pipeline, so they fit three waves per SIMD (three workgroups per CU) with a three-stage ring.
-#ifndef SSW_WPE_SWA
-#define SSW_WPE_SWA 3
-#endif
-#ifndef SSW_STAGES_SWA
-#define SSW_STAGES_SWA 3
-#endif
-#ifndef SSW_PIPELINE_SWA
-#define SSW_PIPELINE_SWA 0
-#endif
-#ifndef SSW_PREFETCH_PARTIAL
-#define SSW_PREFETCH_PARTIAL 1  // gated SA pass: intermediate rows fetched during the last chunk
-#endif
-#ifndef SSW_XCD_REMAP
-#define SSW_XCD_REMAP 1
-#endif
 constexpr int kWave = 64;
-constexpr int kWaves = SSW_WAVES;  // waves per workgroup
+constexpr int kWaves = 4;  // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kColsWave = 32;
 constexpr int kColsWG = kColsWave * kWaves;
 constexpr int kChunk = 32;
-constexpr int kStages = SSW_STAGES;  // LDS ring depth: kStages - 1 chunks in flight
-#ifndef SSW_SIGCAP
-#define SSW_SIGCAP 2048
-#endif
-// SA alone (sigma-gathered, plain store epilogue) has a second build for three waves per SIMD
-// with a 3-slot ring and a 1024-entry sigma segment (3 x 16 KB + 4 KB of LDS per workgroup at
-// bf16/d128, so three workgroups fit a CU).  It is launched when the workgroup's band fits one
-// sigma segment; longer bands use the two-wave build, which holds 2048 entries.
-#ifndef SSW_W3_STORE
-#define SSW_W3_STORE 1
-#endif
-#ifndef SSW_SIGCAP_W3
-#define SSW_SIGCAP_W3 1024
-#endif
-// parts of the register diet of the three-waves causal build at d = 128 (tuning switches).
-// Recomputing the DMA row keys and offsets at each issue fits the last register without a spill
-// but costs more than the one spill outside the loop it avoids (about 8% on causal SA alone),
-// so it is off.
-#ifndef SSW_LEAN_DMA
-#define SSW_LEAN_DMA 0
-#endif
-#ifndef SSW_LEAN_KV
-#define SSW_LEAN_KV 1
-#endif
-#ifndef SSW_LEAN_MASK
-#define SSW_LEAN_MASK 1
-#endif
-constexpr int kSigCap = SSW_SIGCAP;  // sigma entries held in LDS at a time
+// The sigma-gathered kernels have two builds (template flag W3):
+//   * two waves per SIMD (register allocation sized for it), a 4-stage ring (kStages - 1 chunks
+//     in flight) consumed two 32-key chunks per loop step (bf16; fp32 computes the scores of
+//     chunk c + 1 alongside the softmax of chunk c), and a 2048-entry sigma segment;
+//   * bf16 only, three waves per SIMD: a 3-stage ring, one chunk per step and a 1024-entry sigma
+//     segment (3 x 16 KB + 4 KB of LDS per workgroup at d = 128, so three workgroups fit a CU).
+//     The dispatcher launches it when a workgroup's band fits one segment; longer bands use the
+//     two-wave build.  At d = 128 the causal build recomputes the K/V LDS offsets at their use
+//     from one base register each and reads sigma for the mask in two halves, to fit the
+//     registers of three waves.
+// The identity-sigma (SWA) kernels hold no sigma in LDS and fewer registers, so they run at three
+// waves per SIMD with a 3-stage ring and one chunk per step.
+constexpr int kStages = 4;
+constexpr int kWavesPerSimd = 2;
+constexpr int kSigCap = 2048;      // sigma entries held in LDS at a time (two-wave build)
+constexpr int kSigCapW3 = 1024;    // the same, three-waves build
+constexpr int kWavesPerSimdSwa = 3;
+constexpr int kStagesSwa = 3;
 constexpr float kLazy = 8.0f;  // reference max may lag the true max by up to 2^8 (log2 units)
-// bf16 gated path: the SWA pass leaves g_swa * Y_swa in the output buffer as fp16 scaled by 2^-8
+// bf16 gated path: the SA pass leaves g_sa * Y_sa in the output buffer as fp16 scaled by 2^-8
 constexpr float kPartialScale = 1.0f / 256.0f;
 constexpr float kPartialUnscale = 256.0f;
 
@@ -233,11 +195,11 @@ struct Layout {
   static constexpr int kDmaPerWave = 2 * kDmaK / kWaves;
   static constexpr int kStageBytes = 2 * kMatBytes;
   // sigma of a segment of keys (permuted operator only)
-  static constexpr int kSigCapL = W3 ? SSW_SIGCAP_W3 : kSigCap;
+  static constexpr int kSigCapL = W3 ? kSigCapW3 : kSigCap;
   static constexpr int kSegChunks = kSigCapL / kChunk;
   static constexpr int kSigBytes = PERM ? kSigCapL * 4 : 0;
   // ring depth: the configured number of stages, or fewer if they would not fit in 160 KB of LDS
-  static constexpr int kWant = W3 ? 3 : PERM ? kStages : SSW_STAGES_SWA;
+  static constexpr int kWant = W3 ? 3 : PERM ? kStages : kStagesSwa;
   static constexpr int kNS = kWant * kStageBytes + kSigBytes <= 163840
                                  ? kWant
                                  : (163840 - kSigBytes) / kStageBytes;
@@ -260,12 +222,9 @@ __device__ __forceinline__ int swz_k(int row) {
 // granules of the same 4 keys).  For 16-granule rows the XOR values 0, 6, 10, 12 spread both the
 // 16-lane and the 32-lane footprint over distinct bank slots (their residues mod 8 are distinct
 // and so are their bits 2..3); 8-granule rows use 0, 2, 4, 6.
-#ifndef SSW_VSWZ_WIDE
-#define SSW_VSWZ_WIDE 1
-#endif
 template <int GRAN>
 __device__ __forceinline__ int swz_v(int key) {
-  if constexpr (GRAN >= 16 && SSW_VSWZ_WIDE)
+  if constexpr (GRAN >= 16)
     return (int)((0x0C0A0600u >> (8 * (key & 3))) & 0xFFu);
   else
     return 2 * (key & 3);
@@ -293,10 +252,8 @@ struct Params {
 // ids are renumbered to give every XCD a contiguous run of tiles: id i runs tile-major position
 // (i % 8) * (N / 8) + i / 8 (a bijection on the first 8 * floor(N / 8) ids; the rest keep theirs).
 __device__ __forceinline__ int xcd_local_order(int i, int nblocks) {
-#if SSW_XCD_REMAP
   const int per = nblocks / 8;
   if (i < per * 8) return (i % 8) * per + i / 8;
-#endif
   return i;
 }
 
@@ -304,7 +261,7 @@ template <typename T, bool PERM, int EPI, bool W3>
 constexpr bool kIsW3 = W3 && PERM && sizeof(T) == 2;
 template <typename T, bool PERM, int EPI, bool W3>
 constexpr int kWavesPerEU =
-    kIsW3<T, PERM, EPI, W3> ? 3 : (PERM || sizeof(T) != 2) ? SSW_WPE : SSW_WPE_SWA;
+    kIsW3<T, PERM, EPI, W3> ? 3 : (PERM || sizeof(T) != 2) ? kWavesPerSimd : kWavesPerSimdSwa;
 
 template <typename T, int D, bool PERM, bool SIGMASK, int EPI, bool W3>
 __global__ __launch_bounds__(kThreads)
@@ -314,16 +271,15 @@ void band_attn_kernel(Params prm) {
   constexpr bool kW3 = kIsW3<T, PERM, EPI, W3>;
   using Lay = Layout<T, D, PERM, kW3>;
   constexpr int kSegChunks = Lay::kSegChunks;  // chunks per sigma segment
-  constexpr bool kPipe = kW3 ? false : PERM ? SSW_PIPELINE : SSW_PIPELINE_SWA;
+  constexpr bool kPipe = !kW3 && PERM;  // scores of chunk c + 1 beside the softmax of chunk c
   constexpr bool kBf16 = Lay::kBf16;
   // At three waves per SIMD (168 registers) the causal sigma-gathered kernel at d = 128
   // recomputes the K/V LDS offsets at their use (from one base register each) instead of holding
   // them across the loop, and reads sigma for the causal mask in two halves.  (d = 64 fits
   // without.)
   constexpr bool kLeanAny = kW3 && SIGMASK && D == 128;
-  constexpr bool kLeanDma = kLeanAny && SSW_LEAN_DMA;
-  constexpr bool kLean = kLeanAny && SSW_LEAN_KV;  // K/V LDS offsets
-  constexpr bool kLeanMask = kLeanAny && SSW_LEAN_MASK;
+  constexpr bool kLean = kLeanAny;  // K/V LDS offsets
+  constexpr bool kLeanMask = kLeanAny;
   __shared__ __attribute__((aligned(16))) char smem[Lay::kSmem];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;  // LDS byte address of smem
   int* sig_lds = (int*)(smem + Lay::kSigOff);
@@ -403,14 +359,12 @@ void band_attn_kernel(Params prm) {
     const int gran = ln % Lay::kGran;
     return (uint32_t)((gran ^ (isv ? swz_v<Lay::kGran>(row) : swz_k<Lay::kGran>(row))) * 16);
   };
-  int dma_key[kLeanDma ? 1 : kDW];
-  uint32_t dma_goff[kLeanDma ? 1 : kDW];
-  if constexpr (!kLeanDma) {
+  int dma_key[kDW];
+  uint32_t dma_goff[kDW];
 #pragma unroll
-    for (int i = 0; i < kDW; ++i) {
-      dma_key[i] = dma_key_of(i, lane);
-      dma_goff[i] = dma_goff_of(i, lane);
-    }
+  for (int i = 0; i < kDW; ++i) {
+    dma_key[i] = dma_key_of(i, lane);
+    dma_goff[i] = dma_goff_of(i, lane);
   }
   // STAGE is a compile-time ring slot, so LDS addresses fold into instruction offsets.  The sigma
   // reads for all of this wave's rows go out first (unconditionally: the segment's sigma buffer
@@ -422,7 +376,7 @@ void band_attn_kernel(Params prm) {
     DmaRows r;
 #pragma unroll
     for (int i = 0; i < kDW; ++i) {
-      const int q = kc0 + (kLeanDma ? dma_key_of(i, opaque(lane)) : dma_key[i]);
+      const int q = kc0 + dma_key[i];
       r.row[i] = PERM ? sig_lds[q - seg_key0] : q;
     }
     return r;
@@ -438,7 +392,7 @@ void band_attn_kernel(Params prm) {
       const bool isv = I >= Lay::kDmaK;
       const int blkid = isv ? I - Lay::kDmaK : I;
       const uint32_t voff = __umul24((uint32_t)r.row[i], row_stride32) +
-                            (kLeanDma ? dma_goff_of(i, opaque(lane)) : dma_goff[i]);
+                            dma_goff[i];
       const uint32_t lds = smem_lds + STAGE * Lay::kStageBytes + (isv ? Lay::kMatBytes : 0) +
                            blkid * 1024;
       dma16(isv ? rs_v : rs_k, __builtin_amdgcn_readfirstlane(lds), voff);
@@ -450,11 +404,11 @@ void band_attn_kernel(Params prm) {
   // wave's columns i * (1024 / RB) ..., lane l granule l % kGran of column i * (1024 / RB) +
   // l / kGran; granules are XOR-swizzled by column so the epilogue's reads spread over banks.
   // bf16 with a 4-slot ring: two chunks per loop step; the prologue then fetches one step
-  constexpr bool kStep2 = SSW_STEP2 && kPipe && kBf16 && Lay::kNS == 4;
+  constexpr bool kStep2 = kPipe && kBf16 && Lay::kNS == 4;
   constexpr int kPro = kStep2 ? 2 : Lay::kPF;
   // (needs kWaves / 2 ring stages besides the last chunk's)
   constexpr bool kPrefetchPartial =
-      SSW_PREFETCH_PARTIAL && EPI == kEpiAddPartial && kBf16 && Lay::kNS - 1 >= (kWaves + 1) / 2;
+      EPI == kEpiAddPartial && kBf16 && Lay::kNS - 1 >= (kWaves + 1) / 2;
   const int64_t out_batch_bytes = (int64_t)n * prm.Hq * D * (int)sizeof(T);
   const i32x4 rs_out =
       make_rsrc(prm.out + (int64_t)b * out_batch_bytes, (uint32_t)out_batch_bytes);
@@ -1244,36 +1198,32 @@ void band_attn_kernel(Params prm) {
         // granule d0 / 8 of the row, swizzled by column; bytes 8 * h32 within it
         u32x2* slot = (u32x2*)(rowp + 16 * ((d0 >> 3) ^ ((lane & 31) & (Lay::kGran - 1))) +
                                8 * h32);
-        float y[4];
+        // (the intermediate's 2^-8 is a power of two: folded into the factor, it rounds the same)
+        const float fs = EPI == kEpiPartial ? f * kPartialScale : f;
+        f32x2 y[2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) y[u] = o[t][4 * a + u] * f;
+        for (int u = 0; u < 2; ++u) y[u] = f32x2{o[t][4 * a + 2 * u] * fs, o[t][4 * a + 2 * u + 1] * fs};
         uint32_t w[2];
         if constexpr (EPI == kEpiPartial) {
-          // the gated intermediate: fp16 of y * 2^-8 (8x finer than bf16, range 1.6e7)
+          // the gated intermediate: fp16 of y * 2^-8, one packed conversion per pair
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const _Float16 lo = (_Float16)(y[2 * u] * kPartialScale);
-            const _Float16 hi = (_Float16)(y[2 * u + 1] * kPartialScale);
-            w[u] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-          }
+          for (int u = 0; u < 2; ++u)
+            w[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y[u], f16x2));
         } else {
           if constexpr (EPI == kEpiAddPartial) {
-            const u32x2 old = kPrefetchPartial ? *slot : *(const u32x2*)(prm.out +
-                                  (int64_t)b * out_batch_bytes + (rowvalid ? out_off : 0u) +
-                                  d0 * 2);
+            static_assert(kPrefetchPartial, "bf16 intermediate rows come through the ring");
+            const u32x2 old = *slot;
+            // whole-vector casts only: taking the two halves of `old` element by element
+            // (then a per-element cast to fp16 pairs) was miscompiled into one 4-byte read
+            const f32x4 p = __builtin_convertvector(__builtin_bit_cast(f16x4, old), f32x4);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              y[2 * u] += (float)__builtin_bit_cast(_Float16, (uint16_t)(old[u] & 0xffffu)) *
-                          kPartialUnscale;
-              y[2 * u + 1] += (float)__builtin_bit_cast(_Float16, (uint16_t)(old[u] >> 16)) *
-                              kPartialUnscale;
-            }
+            for (int u = 0; u < 2; ++u)
+              y[u] = f32x2{__builtin_fmaf(p[2 * u], kPartialUnscale, y[u][0]),
+                           __builtin_fmaf(p[2 * u + 1], kPartialUnscale, y[u][1])};
           }
 #pragma unroll
           for (int u = 0; u < 2; ++u)
-            w[u] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[2 * u]) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y[2 * u + 1]) << 16);
+            w[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y[u], bf16x2));
         }
         *slot = u32x2{w[0], w[1]};
       }
@@ -1364,7 +1314,7 @@ static hipError_t launch_d(const BandLaunch& a, const Params& prm, hipStream_t s
     // + 1 slots plus L + R keys, fits its 1024-entry sigma segment.
     const int64_t band = (kColsWG + prm.G - 1) / prm.G + 1 + (int64_t)prm.L + prm.R;
     if constexpr (sizeof(T) == 2) {
-      if (SSW_W3_STORE && band <= SSW_SIGCAP_W3) {
+      if (band <= kSigCapW3) {
         if (a.causal)
           return part ? launch_t<T, D, true, true, kEpiPartial, true>(prm, s, e0, e1)
                       : launch_t<T, D, true, true, kEpiStore, true>(prm, s, e0, e1);
