@@ -218,6 +218,21 @@ int ssw_gated_sa_swa_backward(const void* q, const void* k, const void* v, const
                               float* delta, int B, int n, int Hq, int Hkv, int d, int dtype,
                               void* stream);
 
+/* The same backward for callers that cannot allocate memory (code under HIP graph capture, tight
+ * training loops, harnesses that forbid hipMalloc): no delta argument; Delta lives in a device
+ * array of the library itself (16 MiB per GPU, held until the process ends), so the call
+ * allocates nothing.  Limit: B * n * Hq <= 4194304 (2^22), else SSW_ESHAPE.  Every call on one
+ * GPU shares that array, so calls that overlap on one GPU (other streams, other threads) race and
+ * must be ordered by the caller.  The first call on a device looks the array's address up
+ * (SSW_EHIP if that fails).  Other arguments, results and errors as in
+ * ssw_gated_sa_swa_backward. */
+int ssw_gated_sa_swa_backward_noalloc(const void* q, const void* k, const void* v,
+                                      const int32_t* sigma, int window, int causal,
+                                      const float* gates, const void* y_sa, const float* lse_sa,
+                                      const void* y_swa, const float* lse_swa, const void* dout,
+                                      void* dq, void* dk, void* dv, float* dgates, int B, int n,
+                                      int Hq, int Hkv, int d, int dtype, void* stream);
+
 /* ---- Decode: one new token per batch row over a KV cache ----
  *
  * The pages apply SA to pretrained models without training ([SA-ja] 主要な貢献 item 3, 結果),

@@ -21,6 +21,8 @@ Training (bf16):
     swa_backward(q, k, v, window, causal, out, lse, dout, gate=None, ...) -> (dq, dk, dv, dgate)
     gated_sa_swa_forward_train(q, k, v, sigma, window, causal, gates) -> (out, saved)
     gated_sa_swa_backward(q, k, v, sigma, window, causal, gates, saved, dout) -> (dq, dk, dv, dgates)
+    gated_sa_swa_backward_noalloc(q, k, v, sigma, window, causal, gates, saved, dout, dq, dk, dv,
+                                  dgates=None)   (allocates nothing: Delta in the library's array)
 
 Variant: one sigma per batch row and/or KV head (sigma [B, n], [Hkv, n] or [B, Hkv, n]):
 
@@ -58,7 +60,8 @@ __all__ = [
     "SSWError", "LIB_PATH", "sa_forward", "swa_forward", "gated_sa_swa_forward",
     "make_permutation", "inverse_permutation", "check_permutation", "neighbor_mask",
     "last_error", "F32", "BF16", "sa_forward_lse", "swa_forward_lse", "sa_backward",
-    "swa_backward", "gated_sa_swa_forward_train", "gated_sa_swa_backward", "sa_decode",
+    "swa_backward", "gated_sa_swa_forward_train", "gated_sa_swa_backward",
+    "gated_sa_swa_backward_noalloc", "sa_decode",
     "swa_decode", "gated_sa_swa_decode", "sa_forward_ex", "gated_sa_swa_forward_ex",
     "receptive_field_coverage", "gate_projection",
 ]
@@ -117,6 +120,10 @@ def _load() -> ctypes.CDLL:
                                               vp, vp, vp, vp, f32p, f32p, i32, i32, i32, i32, i32,
                                               i32, vp]
     lib.ssw_gated_sa_swa_backward.restype = ctypes.c_int
+    lib.ssw_gated_sa_swa_backward_noalloc.argtypes = [vp, vp, vp, i32p, i32, i32, f32p, vp, f32p,
+                                                      vp, f32p, vp, vp, vp, vp, f32p, i32, i32,
+                                                      i32, i32, i32, i32, vp]
+    lib.ssw_gated_sa_swa_backward_noalloc.restype = ctypes.c_int
     dec = [vp, vp, vp, i32p, i32p, i32p, i32, f32p, vp, i32, i32, i32, i32, i32, i32, vp]
     for name in ("ssw_sa_decode", "ssw_swa_decode", "ssw_gated_sa_swa_decode"):
         fn = getattr(lib, name)
@@ -490,6 +497,34 @@ def gated_sa_swa_backward(q, k, v, sigma, window: int, causal: bool, gates, save
         _dev_ptr(gates), _dev_ptr(y_sa), _dev_ptr(lse_sa), _dev_ptr(y_swa), _dev_ptr(lse_swa),
         _dev_ptr(dout), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv), _dev_ptr(dgates),
         _dev_ptr(delta), B, n, Hq, k.shape[2], d, _dtype_code(q), _stream_handle(q)))
+    return dq, dk, dv, dgates
+
+
+def gated_sa_swa_backward_noalloc(q, k, v, sigma, window: int, causal: bool, gates, saved, dout,
+                                  dq, dk, dv, dgates=None):
+    """ssw_gated_sa_swa_backward_noalloc: the gated layer's backward with Delta in the library's
+    own device array, so the call allocates nothing (dq, dk, dv and, if wanted, dgates are the
+    caller's; B * n * Hq <= 2^22).  Returns (dq, dk, dv, dgates)."""
+    torch = _torch()
+    _prep(q, k, v, None)
+    B, n, Hq, d = q.shape
+    sigma = _prep_sigma(sigma, n, q.device)
+    gates = _prep_gate(gates, (2, B, n, Hq), q.device)
+    if gates is None:
+        raise ValueError("gates are required")
+    y_sa, lse_sa, y_swa, lse_swa = saved
+    y_sa, y_swa = _prep_like(y_sa, q, "y_sa"), _prep_like(y_swa, q, "y_swa")
+    lse_sa = _prep_rows(lse_sa, (B, n, Hq), torch.float32, q.device, "lse_sa")
+    lse_swa = _prep_rows(lse_swa, (B, n, Hq), torch.float32, q.device, "lse_swa")
+    dout = _prep_like(dout, q, "dout")
+    dq, dk, dv = _prep_like(dq, q, "dq"), _prep_like(dk, k, "dk"), _prep_like(dv, v, "dv")
+    if dgates is not None:
+        dgates = _prep_rows(dgates, (2, B, n, Hq), torch.float32, q.device, "dgates")
+    _check(_lib.ssw_gated_sa_swa_backward_noalloc(
+        _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sigma), int(window), int(bool(causal)),
+        _dev_ptr(gates), _dev_ptr(y_sa), _dev_ptr(lse_sa), _dev_ptr(y_swa), _dev_ptr(lse_swa),
+        _dev_ptr(dout), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv), _dev_ptr(dgates), B, n, Hq,
+        k.shape[2], d, _dtype_code(q), _stream_handle(q)))
     return dq, dk, dv, dgates
 
 

@@ -73,6 +73,11 @@ struct BandBwdLaunch {
 
 hipError_t launch_band_attn_bwd(const BandBwdLaunch& a, hipStream_t stream);
 
+// The library's own Delta array for the backward entry point that allocates nothing: entries
+// (B * n * Hq at most), and its device address on the current device (looked up once per device).
+constexpr int64_t kBwdScratchFloats = int64_t(1) << 22;  // 16 MiB
+hipError_t bwd_scratch_pointer(float** ptr);
+
 // One decode step per batch row over a KV cache (SA and/or SWA, optionally gated).
 struct DecodeLaunch {
   const void* q;          // [B, Hq, d]

@@ -31,6 +31,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "band_attn.h"
 #include "lds_dma.h"
 
@@ -751,6 +753,33 @@ static hipError_t launch_d(const BandBwdLaunch& a, const Params& prm, hipStream_
 }
 
 }  // namespace bwd
+
+// ---- Delta without allocation: a device array of this library (one copy per GPU, held until the
+// process ends) for callers that cannot allocate memory.  Its name is a host-side stand-in for the
+// array, not a device address: host code reaches the array only through the address that
+// hipGetSymbolAddress returns for the current device, which is looked up on the first call on
+// each device and kept.  Every call on one GPU shares the array: calls that overlap on one GPU
+// race.  The dQ kernel writes every entry the dK/dV kernel reads, so nothing needs clearing.
+static __device__ __align__(256) float scratch[kBwdScratchFloats];
+
+hipError_t bwd_scratch_pointer(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = (float*)p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_band_attn_bwd(const BandBwdLaunch& a, hipStream_t stream) {
   bwd::Params prm;

@@ -459,15 +459,26 @@ int ssw_gated_sa_swa_forward_train(const void* q, const void* k, const void* v,
   return SSW_OK;
 }
 
-int ssw_gated_sa_swa_backward(const void* q, const void* k, const void* v, const int32_t* sigma,
-                              int window, int causal, const float* gates, const void* y_sa,
-                              const float* lse_sa, const void* y_swa, const float* lse_swa,
-                              const void* dout, void* dq, void* dk, void* dv, float* dgates,
-                              float* delta, int B, int n, int Hq, int Hkv, int d, int dtype,
-                              void* stream) {
-  const char* who = "ssw_gated_sa_swa_backward";
-  int st = check_backward(who, q, k, v, y_sa, dout, lse_sa, dq, dk, dv, delta, window, causal, B,
-                          n, Hq, Hkv, d, dtype);
+// The gated layer's backward (both entry points): checks, then the SA path (writes the
+// gradients) and the SWA path (adds to them); each path's Delta is consumed by its own dK/dV
+// kernel before the next path overwrites it (stream order).  With delta NULL the library's own
+// array is used (the entry point that allocates nothing).
+static int gated_backward(const char* who, const void* q, const void* k, const void* v,
+                          const int32_t* sigma, int window, int causal, const float* gates,
+                          const void* y_sa, const float* lse_sa, const void* y_swa,
+                          const float* lse_swa, const void* dout, void* dq, void* dk, void* dv,
+                          float* dgates, float* delta, int B, int n, int Hq, int Hkv, int d,
+                          int dtype, void* stream) {
+  const bool own = delta == nullptr;
+  if (own && B > 0 && n > 0 && (int64_t)B * n * Hq > ssw::kBwdScratchFloats)
+    return fail(SSW_ESHAPE, std::string(who) + ": B * n * Hq must be <= " +
+                                std::to_string(ssw::kBwdScratchFloats) +
+                                " (the size of the library's Delta array)");
+  // (the library's array stands in for delta in the argument checks; its device address is only
+  // looked up once they have passed)
+  static const float kStandIn = 0.f;
+  int st = check_backward(who, q, k, v, y_sa, dout, lse_sa, dq, dk, dv, own ? &kStandIn : delta,
+                          window, causal, B, n, Hq, Hkv, d, dtype);
   if (st != SSW_OK || B == 0 || n == 0) return st;
   if (!sigma || !gates || !y_swa || !lse_swa)
     return fail(SSW_EINVAL, std::string(who) + ": sigma, gates, y_swa and lse_swa must be non-NULL");
@@ -480,9 +491,13 @@ int ssw_gated_sa_swa_backward(const void* q, const void* k, const void* v, const
     st = check_sigma_on_device(sigma, n, s);
     if (st != SSW_OK) return st;
   }
+  if (own) {
+    hipError_t e = ssw::bwd_scratch_pointer(&delta);
+    if (e != hipSuccess)
+      return fail(SSW_EHIP, std::string(who) + ": device address of the Delta array: " +
+                                hipGetErrorString(e));
+  }
   const size_t plane = (size_t)B * n * Hq;
-  // SA path first (writes the gradients), then the SWA path (adds to them); each pass's Delta
-  // is consumed by its own dK/dV kernel before the next pass overwrites it (stream order)
   ssw::BandBwdLaunch a1 = make_bwd(q, k, v, sigma, window, causal, gates, y_sa, lse_sa, dout, dq,
                                    dk, dv, dgates, delta, false, B, n, Hq, Hkv, d);
   ssw::BandBwdLaunch a2 =
@@ -490,6 +505,30 @@ int ssw_gated_sa_swa_backward(const void* q, const void* k, const void* v, const
                dgates ? dgates + plane : nullptr, delta, true, B, n, Hq, Hkv, d);
   if ((st = run_bwd(who, a1, s)) != SSW_OK) return st;
   return run_bwd(who, a2, s);
+}
+
+int ssw_gated_sa_swa_backward(const void* q, const void* k, const void* v, const int32_t* sigma,
+                              int window, int causal, const float* gates, const void* y_sa,
+                              const float* lse_sa, const void* y_swa, const float* lse_swa,
+                              const void* dout, void* dq, void* dk, void* dv, float* dgates,
+                              float* delta, int B, int n, int Hq, int Hkv, int d, int dtype,
+                              void* stream) {
+  const char* who = "ssw_gated_sa_swa_backward";
+  if (!delta && B > 0 && n > 0)
+    return fail(SSW_EINVAL, std::string(who) + ": delta must be non-NULL");
+  return gated_backward(who, q, k, v, sigma, window, causal, gates, y_sa, lse_sa, y_swa, lse_swa,
+                        dout, dq, dk, dv, dgates, delta, B, n, Hq, Hkv, d, dtype, stream);
+}
+
+int ssw_gated_sa_swa_backward_noalloc(const void* q, const void* k, const void* v,
+                                      const int32_t* sigma, int window, int causal,
+                                      const float* gates, const void* y_sa, const float* lse_sa,
+                                      const void* y_swa, const float* lse_swa, const void* dout,
+                                      void* dq, void* dk, void* dv, float* dgates, int B, int n,
+                                      int Hq, int Hkv, int d, int dtype, void* stream) {
+  return gated_backward("ssw_gated_sa_swa_backward_noalloc", q, k, v, sigma, window, causal, gates,
+                        y_sa, lse_sa, y_swa, lse_swa, dout, dq, dk, dv, dgates, nullptr, B, n, Hq,
+                        Hkv, d, dtype, stream);
 }
 
 // ---- decode: one new token per batch row over a KV cache

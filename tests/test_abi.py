@@ -239,6 +239,25 @@ def test_gated_training_checks():
     assert bwd(dtype=0) == -3
 
 
+def test_gated_backward_noalloc_checks():
+    """The backward that allocates nothing: the same argument checks (made before any HIP call),
+    and its size limit, B * n * Hq <= 2^22 (the library's own Delta array)."""
+    fn = _lib.ssw_gated_sa_swa_backward_noalloc
+    fn.argtypes = [_VP] * 4 + [_I] * 2 + [_VP] * 10 + [_I] * 6 + [_VP]
+    fn.restype = _I
+    bwd = lambda **kw: fn(
+        P, P, P, kw.get("sigma", P), 8, 1, P, P, P, kw.get("y_swa", P), P, P, P, P, P,
+        kw.get("dgates", None), kw.get("B", 1), kw.get("n", 64), kw.get("Hq", 4), 2, 64,
+        kw.get("dtype", 1), None)
+    assert bwd(sigma=None) == -1
+    assert bwd(y_swa=None) == -1
+    assert bwd(dgates=P + 1) == -4
+    assert bwd(dtype=0) == -3
+    assert bwd(B=0) == 0 and bwd(n=0) == 0
+    assert bwd(B=2, n=65536, Hq=34) == -2
+    assert "Delta array" in ssw.last_error()
+
+
 # ---- decode entry points -----------------------------------------------------------------------
 
 for _n in ("ssw_sa_decode", "ssw_swa_decode", "ssw_gated_sa_swa_decode"):
