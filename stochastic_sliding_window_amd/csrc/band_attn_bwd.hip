@@ -17,15 +17,16 @@
 //     second kernel.  Its loop streams the band's 32-key K/V chunks: S^T = K Q^T and
 //     dP^T = V (dy)^T share the row-read A operands, and dQ^T += K^T dS^T takes K^T from
 //     transposed LDS reads, with dS^T already in B-operand order.
-//   * bwd_dkdv_kernel is key-major: a wave owns 32 key slots of one KV head (their K and V rows
-//     are B operands in registers), the workgroup 128.  Its loop streams chunks of 32 query
-//     columns (Q and dy rows plus each column's log-sum-exp, Delta, gate, slot and original
-//     index): S = Q K^T and dP = dy V^T leave P and dS with one key per lane, which is the B
-//     operand of dV^T += (dy)^T (g P) and dK^T += Q^T dS.
-//   * Chunks are gathered through sigma into registers one chunk ahead and written to a
-//     two-stage LDS ring.  Rows sit in MFMA row order, XOR-swizzled by 16-byte granule, which
-//     serves the row reads of the score products and the transposed reads (ds_read_b64_tr_b16)
-//     of the gradient products alike.
+//   * bwd_dkdv_kernel is key-major: a wave owns 32 key slots of one KV head (their K rows are B
+//     operands in registers, their V rows sit in LDS), the workgroup 128.  Its loop streams
+//     chunks of 32 query columns (Q and dy rows plus each column's log-sum-exp, Delta, gate,
+//     slot and original index): S = Q K^T and dP = dy V^T leave P and dS with one key per lane,
+//     which is the B operand of dV^T += (dy)^T (g P) and dK^T += Q^T dS.
+//   * Chunks are gathered through sigma by direct buffer-to-LDS loads into an LDS ring (three
+//     chunks ahead in the dQ kernel, one in the dK/dV kernel).  Rows sit in MFMA row order, their
+//     16-byte granules XOR-swizzled by a function of the row (Lay::swz), which keeps both the row
+//     reads of the score products and the transposed reads (ds_read_b64_tr_b16) of the gradient
+//     products free of bank conflicts.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <limits.h>
@@ -184,12 +185,29 @@ struct Lay {
   static constexpr int kKB = D / 16;                 // k steps of the score products
   static constexpr int kDB = D / 32;                 // 32-row d blocks of a gradient accumulator
   static_assert(kPer >= 1 && 2 * kChunk * kGran == kPer * kThreads, "chunk split");
+  // Granule g of MFMA row r sits at granule position g ^ swz(r) of its row.  The reads that
+  // must not collide on LDS banks:
+  //  * row reads (16 bytes per lane, 16 lanes per cycle): rows r .. r + 15, one granule each;
+  //  * transposed reads (8 bytes per lane, 32 lanes per cycle): four rows 4a .. 4a + 3 (rows
+  //    rho(e) of four consecutive entries e) times four consecutive granules 4b .. 4b + 3.
+  // 256-byte rows (d = 128) span all 64 banks: swz(r) swaps the two 2-bit halves of r % 16,
+  // which is one-to-one on r % 16 (row reads) and gives the rows 4a + i the values 4i + const, so
+  // that g ^ swz(r) = 4(b ^ i) + (g % 4 ^ const) takes 16 distinct values (transposed reads).
+  // 128-byte rows (d = 64) pair up on the banks, rows 2m and 2m + 1 side by side: swz(r) is bits
+  // 1, 2, 3 of r in reverse order, one-to-one on m % 8 (row reads), and rows 4a, 4a + 2 (the
+  // same bank half) differ in bit 2 of swz, which moves granules 4b .. 4b + 3 to the other four.
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (kGran == 16)
+      return ((r & 3) << 2) | ((r >> 2) & 3);
+    else
+      return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+  }
 };
 
 // LDS offset of granule `gran` of MFMA row `row` within a stage matrix
 template <int D>
 __device__ __forceinline__ int gran_off(int row, int gran) {
-  return row * Lay<D>::kRowBytes + ((gran ^ (row & (Lay<D>::kGran - 1))) << 4);
+  return row * Lay<D>::kRowBytes + ((gran ^ Lay<D>::swz(row)) << 4);
 }
 
 // Per-lane LDS offsets of the transposed reads of a stage matrix.  The A operand of a gradient
@@ -205,7 +223,7 @@ __device__ __forceinline__ int tr_off(int lane, int db, int hi) {
   const int e = 8 * (lane >> 5) + 4 * hi + (j >> 2);
   const int row = rho(e);
   const int d = 32 * db + 16 * (grp & 1) + 4 * (j & 3);
-  return row * Lay<D>::kRowBytes + (((d >> 3) ^ (row & (Lay<D>::kGran - 1))) << 4) + ((d & 7) << 1);
+  return row * Lay<D>::kRowBytes + (((d >> 3) ^ Lay<D>::swz(row)) << 4) + ((d & 7) << 1);
 }
 
 __device__ __forceinline__ bf16x8 tr_read(const char* lo_p, const char* hi_p) {
@@ -301,7 +319,7 @@ void bwd_dq_kernel(Params prm) {
     const int I = wave * kDW + i;
     const int row = kRowsPerDma * (I % kDmaMat) + lane / LY::kGran;
     dma_row[i] = row;
-    dma_goff[i] = (uint32_t)((((lane % LY::kGran) ^ (row & (LY::kGran - 1)))) << 4);
+    dma_goff[i] = (uint32_t)(((lane % LY::kGran) ^ LY::swz(row)) << 4);
   }
   int seg_key0 = kbeg;  // first key of the current sigma segment
   auto orig_of_key = [&](int key) { return PERM ? sig_lds[key - seg_key0] : key; };
@@ -420,16 +438,25 @@ void bwd_dq_kernel(Params prm) {
                                                      0);
       }
       const int kc0 = kbeg + c * kChunk;
+      // dS of the lane's 16 scores, four keys at a time (registers 4qd .. 4qd + 3 hold keys
+      // e0 .. e0 + 3): their sigma arrives as one 16-byte read and the mask is a select (exp2
+      // runs for masked scores too), so that no element waits on an LDS read of its own.
       bf16x8 dsb[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int e = 16 * (r >> 3) + 8 * h32 + (r & 7);
-        const int key = kc0 + e;
-        bool ok = key >= myslot - L && key <= myslot + R && key < n;
-        if constexpr (SIGMASK) ok = ok && sig_lds[key - seg_key0] <= myorig;
-        const float p =
-            ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -lse2)) : 0.f;
-        dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gate_v, dp[r], -delta));
+      for (int qd = 0; qd < 4; ++qd) {
+        const int e0 = 16 * (qd >> 1) + 8 * h32 + 4 * (qd & 1);
+        u32x4 sg4 = {0, 0, 0, 0};
+        if constexpr (SIGMASK) sg4 = *(const u32x4*)(sig_lds + (kc0 + e0 - seg_key0));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * qd + u;
+          const int key = kc0 + e0 + u;
+          bool ok = (key >= myslot - L) & (key <= myslot + R) & (key < n);
+          if constexpr (SIGMASK) ok = ok & ((int)sg4[u] <= myorig);
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -lse2));
+          const float p = ok ? x : 0.f;
+          dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gate_v, dp[r], -delta));
+        }
       }
       // dQ^T[d][col] += K^T[d][key] dS^T[key][col]
 #pragma unroll
@@ -468,7 +495,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void bwd_dkdv_kernel(Params prm) {
   using LY = Lay<D>;
   // per stage: Q rows, dy rows, then per column lse, Delta, gate (64 floats each: a 4-byte DMA
-  // covers 64 lanes), slot, original index
+  // covers 64 lanes), then 64 ints whose upper 32 hold the columns' original indices
   constexpr int kMetaOff = 2 * LY::kMat;
   constexpr int kStage = kMetaOff + 3 * 64 * 4 + 2 * kChunk * 4;
   constexpr int kSlotOff = kMetaOff + 3 * 64 * 4;
@@ -575,7 +602,7 @@ void bwd_dkdv_kernel(Params prm) {
       uint32_t voff = lds_dma::kOutOfRange;
       if (c0 + e < nG)  // columns past the end read as zeros; their band test fails
         voff = (uint32_t)col_row(slot0, rem0, e, slot) * LY::kRowBytes +
-               (uint32_t)((((lane % LY::kGran) ^ (row & (LY::kGran - 1)))) << 4);
+               (uint32_t)(((lane % LY::kGran) ^ LY::swz(row)) << 4);
       lds_dma::load16(I < kDmaMat ? rs_q : rs_d,
                       st_lds + (I / kDmaMat) * LY::kMat + (I % kDmaMat) * 1024, voff);
     }
@@ -586,16 +613,10 @@ void bwd_dkdv_kernel(Params prm) {
       if (lane < kChunk && c0 + lane < nG) moff = (uint32_t)col_row(slot0, rem0, lane, slot) * 4u;
       lds_dma::load4(rs_m, st_lds + kMetaOff + wave * 256, moff);
     }
-    if (tid < kChunk) {
+    if (SIGMASK && tid < kChunk) {
       int* mi = (int*)(smem + (c & 1) * kStage + kSlotOff);
-      if (c0 + tid < nG) {
-        const int ds = div_small(rem0 + tid, prm.inv_g);
-        mi[tid] = slot0 + ds;
-        mi[kChunk + tid] = orig_of_slot(slot0 + ds);  // the column's token: its original index
-      } else {
-        mi[tid] = INT_MIN / 4;  // no key passes the band test (q <= slot + R fails)
-        mi[kChunk + tid] = -1;
-      }
+      // the column's token, its original index (columns past the end fail the band test)
+      mi[kChunk + tid] = c0 + tid < nG ? orig_of_slot(slot0 + div_small(rem0 + tid, prm.inv_g)) : -1;
     }
   };
 
@@ -605,6 +626,18 @@ void bwd_dkdv_kernel(Params prm) {
     dk[db] = zero16();
     dv[db] = zero16();
   }
+
+  const int a_base = gran_off<D>(r32, h32);
+  const int t_base0 = tr_off<D>(lane, 0, 0);
+  const int t_base1 = tr_off<D>(lane, 0, 1);
+  // The band test in column space: column col_lo + x is in the band of the lane's key when its
+  // slot (col_lo + x) / G lies in [myk - R, myk + L] and the column exists (col_lo + x < nG),
+  // i.e. band_lo <= x <= band_hi.
+  const int band_lo = (myk - R) * G - col_lo;
+  const int band_hi = min(myk + L + 1, n) * G - 1 - col_lo;
+  // Without a gate the stages' gate entries hold 1 (the gate DMA never writes them).
+  if (!prm.gate && tid < 2 * kChunk)
+    *(float*)(smem + (tid / kChunk) * kStage + kMetaOff + 128 * 4 + (tid % kChunk) * 4) = 1.0f;
 
   if constexpr (PERM) {
     load_sigma_seg(seg_s0);
@@ -628,21 +661,24 @@ void bwd_dkdv_kernel(Params prm) {
     if (!wave_on || c < c_first || c > c_last) continue;
     const char* Qst = smem + st * kStage;
     const char* Dst = Qst + LY::kMat;
-    // The per-lane LDS offsets are recomputed here from a lane index the optimiser cannot see
-    // through (so it cannot hoist them out of the loop): holding them would spill registers.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    // Per-lane LDS offsets, from two base offsets held across the loop: the row read of k step
+    // kb is a_base ^ (kb << 5) and the transposed read of d block db and half hi is
+    // t_base[hi] ^ (db << 6) (the k step and the d block enter the granule index in bits the row
+    // and its swizzle leave alone).  Opaque copies per chunk keep the optimiser from holding all
+    // sixteen offsets in registers.
+    int ab = a_base, tb0 = t_base0, tb1 = t_base1;
+    asm volatile("" : "+v"(ab), "+v"(tb0), "+v"(tb1));
     int a_off[LY::kKB];
 #pragma unroll
-    for (int kb = 0; kb < LY::kKB; ++kb) a_off[kb] = gran_off<D>(ln & 31, 2 * kb + (ln >> 5));
+    for (int kb = 0; kb < LY::kKB; ++kb) a_off[kb] = ab ^ (kb << 5);
     int t_off[LY::kDB][2];
 #pragma unroll
     for (int db = 0; db < LY::kDB; ++db) {
-      t_off[db][0] = tr_off<D>(ln, db, 0);
-      t_off[db][1] = tr_off<D>(ln, db, 1);
+      t_off[db][0] = tb0 ^ (db << 6);
+      t_off[db][1] = tb1 ^ (db << 6);
     }
     const float* mf = (const float*)(Qst + kMetaOff);  // lse [0, 64), Delta [64, ..), gate
-    const int* mi = (const int*)(Qst + kSlotOff);        // slot [0, 32), original index [32, 64)
+    const int* mi = (const int*)(Qst + kSlotOff);        // original index at [32, 64)
 
     // S[col][key] = <Q, K>, dP[col][key] = <dy, V>; output register i of lane half h32 holds
     // column 16(i / 8) + 8h32 + i % 8 of the chunk, for the lane's key
@@ -654,19 +690,40 @@ void bwd_dkdv_kernel(Params prm) {
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(Dst + a_off[kb]),
                                                    ld_bf16x8(vrows + a_off[kb]), dp, 0, 0, 0);
     }
+    // P and dS of the lane's 16 scores, four columns at a time: registers 4qd .. 4qd + 3 hold
+    // columns x = e0 + 8 h32 + u (e0 = 16 (qd / 2) + 4 (qd % 2)).  Each group's log-sum-exp,
+    // Delta, gate and original indices arrive as 16-byte reads and the mask is a select (exp2
+    // runs for masked scores too), so that no score waits on an LDS read of its own.  Each
+    // group's reads are issued after the previous group's results (an empty asm ties their
+    // address to them): all sixteen scores' values at once would not fit in the registers.
+    const int lo = band_lo - c * kChunk - 8 * h32;
+    const int hi = band_hi - c * kChunk - 8 * h32;
+    int moff = 32 * h32;  // byte offset of the lane half's first column in each metadata array
     bf16x8 pb[2], dsb[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int e = 16 * (r >> 3) + 8 * h32 + (r & 7);
-      const int slot = mi[e];
-      bool ok = myk >= slot - L && myk <= slot + R;
-      if constexpr (SIGMASK) ok = ok && ktok <= mi[kChunk + e];
-      const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2,
-                                                                 -mf[e] * kLog2e))
-                         : 0.f;
-      const float gt = prm.gate ? mf[128 + e] : 1.0f;
-      pb[r >> 3][r & 7] = (__bf16)(p * gt);
-      dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gt, dp[r], -mf[64 + e]));
+    for (int qd = 0; qd < 4; ++qd) {
+      const int e0 = 16 * (qd >> 1) + 4 * (qd & 1);
+      const char* mq = (const char*)mf + moff + 4 * e0;
+      const f32x4 lse4 = *(const f32x4*)(mq);
+      const f32x4 del4 = *(const f32x4*)(mq + 64 * 4);
+      const f32x4 gt4 = *(const f32x4*)(mq + 128 * 4);
+      u32x4 or4 = {0, 0, 0, 0};
+      if constexpr (SIGMASK) or4 = *(const u32x4*)((const char*)mi + kChunk * 4 + moff + 4 * e0);
+      float last = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * qd + u;
+        bool ok = (e0 + u >= lo) & (e0 + u <= hi);
+        if constexpr (SIGMASK) ok = ok & (ktok <= (int)or4[u]);
+        const float x =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -lse4[u] * kLog2e));
+        const float p = ok ? x : 0.f;
+        const float pg = p * gt4[u];
+        pb[r >> 3][r & 7] = (__bf16)pg;
+        dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gt4[u], dp[r], -del4[u]));
+        last = pg;
+      }
+      asm volatile("" : "+v"(moff) : "v"(last));
     }
     // dV^T[d][key] += dy^T[d][col] (g P)[col][key];  dK^T[d][key] += Q^T[d][col] dS[col][key]
 #pragma unroll

@@ -121,6 +121,24 @@ def test_backward_matches_oracle(shape, path, causal, gated):
          f"dq/dk/dv/dg rel {errs[0]:.2e}/{errs[1]:.2e}/{errs[2]:.2e}/{errs[3]:.2e}")
 
 
+# Larger grids (256 and more workgroups per kernel, several per CU in flight) with ragged last
+# tiles (1100 = 8 * 128 + 76, 800 = 6 * 128 + 32), d = 64 and d = 128
+LARGER = [
+    ((4, 1100, 16, 16, 64, 40), "sa", True, False),
+    ((4, 1100, 16, 16, 64, 40), "sa", False, True),
+    ((4, 1100, 16, 16, 64, 40), "swa", True, True),
+    ((2, 800, 64, 32, 128, 30), "sa", True, True),
+    ((2, 800, 64, 32, 128, 30), "swa", False, False),
+]
+
+
+@pytest.mark.parametrize("shape,path,causal,gated", LARGER,
+                         ids=lambda c: _ids(c) if isinstance(c, tuple) else str(c))
+def test_backward_larger_grids(shape, path, causal, gated):
+    """Every gradient of every row against the oracle on grids of hundreds of workgroups."""
+    test_backward_matches_oracle(shape, path, causal, gated)
+
+
 def test_forward_lse_output_equals_inference_forward():
     B, n, Hq, Hkv, d, w = 1, 700, 8, 2, 128, 64
     host, (q, k, v, g, dy) = _inputs(11, B, n, Hq, Hkv, d)

@@ -120,12 +120,12 @@ def _np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_sa_backward_band_over_two_sigma_segments(causal):
+@pytest.mark.parametrize("causal,B", [(True, 1), (False, 1), (True, 8)])
+def test_sa_backward_band_over_two_sigma_segments(causal, B):
     """dq of sampled query rows and (causal) dk, dv of sampled key rows of SA with a gate, at a
     band over two sigma segments of the dQ (2231 keys per tile) and dK/dV (128 + 2198 query
-    slots per tile) kernels."""
-    B, n, Hq, Hkv, d, w = 1, 4096, 8, 2, 128, W_LONG
+    slots per tile) kernels; B = 8 also checks batch rows past the first."""
+    n, Hq, Hkv, d, w = 4096, 8, 2, 128, W_LONG
     seed = 8300 + (1 if causal else 0)
     q, k, v = synth.qkv(seed, B, n, Hq, Hkv, d, "bf16")
     g = synth.gates(seed, B, n, Hq)
