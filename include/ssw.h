@@ -89,11 +89,13 @@ int ssw_swa_forward(const void* q, const void* k, const void* v, const int32_t* 
  * Two kernels run back to back on `stream`: the SA pass leaves g_sa (.) Y_sa in `out` as an
  * intermediate, at the scattered rows sigma[p], then the SWA pass reads it at its own rows, adds
  * g_swa (.) Y_swa and stores the sum.  For fp32 the intermediate is fp32.  For bf16 it is held,
- * in the same two bytes per element, as fp16 bits of g_sa (.) Y_sa * 2^-8, so the result is in
- * effect rounded to bf16 once: for |g_sa (.) Y_sa| >= 2^-6 that keeps 3 more significand bits
- * than bf16, below it the step is a fixed 2^-16 (absolute error <= 2^-17 = 7.6e-6); it needs
- * |g_sa (.) Y_sa| < 1.6e7 (true whenever |V| < 1.6e7).  Between the two passes `out` holds that
- * intermediate, not a result.  Other arguments as in ssw_sa_forward. */
+ * in the same two bytes per element, as fp16 bits of g_sa (.) Y_sa * 2^-4, so the result is in
+ * effect rounded to bf16 once: for |g_sa (.) Y_sa| >= 2^-10 that keeps 3 more significand bits
+ * than bf16; below it the step is a fixed 2^-20 (absolute error <= 2^-21 = 4.8e-7), as fine as
+ * bf16's own step down to |g_sa (.) Y_sa| = 2^-13.  It needs |g_sa (.) Y_sa| < 1.05e6 (true
+ * whenever |V| < 1.05e6: Y is a convex combination of V rows); larger values become infinite.
+ * Between the two passes `out` holds that intermediate, not a result.  Other arguments as in
+ * ssw_sa_forward. */
 int ssw_gated_sa_swa_forward(const void* q, const void* k, const void* v, const int32_t* sigma,
                              int window, int causal, const float* gates, void* out,
                              int B, int n, int Hq, int Hkv, int d, int dtype, void* stream);
@@ -278,13 +280,21 @@ int ssw_make_permutation(uint64_t seed, int n, int32_t* sigma_out, int32_t* inv_
  * permutation of [0, n). */
 int ssw_inverse_permutation(const int32_t* sigma, int n, int32_t* inv_out);
 
-/* SSW_OK if sigma (host) is a permutation of [0, n), else SSW_ENOTPERM. */
+/* SSW_OK if sigma (host int32[n]) is a permutation of [0, n), else SSW_ENOTPERM.  [SA-ja]
+ * 中核メカニズム step 1 draws sigma uniformly from the permutations of the n positions, so the
+ * forward calls take sigma to be one (they trust it unless SSW_VALIDATE=1 makes them run this
+ * check first).  No GPU; sigma is not modified; n >= 0. */
 int ssw_check_permutation(const int32_t* sigma, int n);
 
-/* Debug: neighbour sets as a bitmask, computed on the device with the same membership test the
- * attention kernels use.  bits (device uint32 [n][ceil(n/32)], fully overwritten): bit j of row i
- * is set iff original token i attends to original token j.  sigma (device int32[n]) or NULL for
- * SWA.  Meant for small n (n <= 4096). */
+/* Debug: the random neighbourhood of every token ([SA-ja] 中核メカニズム: the neighbours of
+ * token i are the tokens whose permuted slots lie within w - 1 of i's slot, and in causal mode
+ * only those not after i; with sigma NULL the SWA window of [HYB] ハイブリッドアーキテクチャの
+ * 定義), as a bitmask computed on the device with the membership test the attention kernels use.
+ * bits (device uint32 [n][ceil(n/32)], owned by the caller, fully overwritten): bit j of row i is
+ * set iff original token i attends to original token j.  sigma: device int32[n] or NULL.
+ * Enqueued on `stream`.  Errors: SSW_EINVAL (n < 0, window < 1, causal not 0 or 1, bits NULL),
+ * SSW_ESHAPE (n > 65536: the mask takes n^2 / 8 bytes; meant for small n), SSW_EALIGN (sigma or
+ * bits not 4-byte aligned), SSW_EHIP (a launch failed). */
 int ssw_neighbor_mask(const int32_t* sigma, int n, int window, int causal, uint32_t* bits,
                       void* stream);
 
@@ -301,7 +311,9 @@ int ssw_neighbor_mask(const int32_t* sigma, int n, int window, int causal, uint3
 int ssw_receptive_field_coverage(int n, int window, int layers, const uint64_t* seeds, int mode,
                                  int causal, double* coverage_out);
 
-/* Message describing the most recent failed call on the calling thread ("" if none). */
+/* Message describing the most recent failed call on the calling thread ("" if none).  The string
+ * belongs to the library (thread-local storage) and stays valid until that thread's next failed
+ * call; it is not a passage of the method but the error channel of every entry point above. */
 const char* ssw_last_error(void);
 
 #ifdef __cplusplus

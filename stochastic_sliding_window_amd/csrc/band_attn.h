@@ -11,8 +11,8 @@ namespace ssw {
 //   kEpiStore:      store it in the output dtype.
 //   kEpiPartial:    store it as the gated layer's intermediate (its first pass, the
 //                   sigma-gathered SA pass): fp32 for fp32 outputs; for bf16 outputs, fp16 bits
-//                   of Y * 2^-8 in the same two bytes (holds |Y| < 1.6e7; 3 more significand
-//                   bits than bf16 for |Y| >= 2^-6, a fixed 2^-16 step below that).
+//                   of Y * 2^-4 in the same two bytes (holds |Y| < 1.05e6; 3 more significand
+//                   bits than bf16 for |Y| >= 2^-10, a fixed 2^-20 step below that).
 //   kEpiAddPartial: read that intermediate, add, store in the output dtype (the gated layer's
 //                   second pass, plain SWA with sigma = identity).
 enum Epilogue { kEpiStore = 0, kEpiPartial = 1, kEpiAddPartial = 2 };

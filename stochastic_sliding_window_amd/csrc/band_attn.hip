@@ -85,9 +85,10 @@ constexpr int kSigCapW3 = 1024;    // the same, three-waves build
 constexpr int kWavesPerSimdSwa = 3;
 constexpr int kStagesSwa = 3;
 constexpr float kLazy = 8.0f;  // reference max may lag the true max by up to 2^8 (log2 units)
-// bf16 gated path: the SA pass leaves g_sa * Y_sa in the output buffer as fp16 scaled by 2^-8
-constexpr float kPartialScale = 1.0f / 256.0f;
-constexpr float kPartialUnscale = 256.0f;
+// bf16 gated path: the SA pass leaves g_sa * Y_sa in the output buffer as fp16 scaled by 2^-4
+// (normal fp16 for 2^-10 <= |g_sa * Y_sa| < 1.05e6; a fixed 2^-20 step below that range)
+constexpr float kPartialScale = 1.0f / 16.0f;
+constexpr float kPartialUnscale = 16.0f;
 
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
@@ -1198,14 +1199,14 @@ void band_attn_kernel(Params prm) {
         // granule d0 / 8 of the row, swizzled by column; bytes 8 * h32 within it
         u32x2* slot = (u32x2*)(rowp + 16 * ((d0 >> 3) ^ ((lane & 31) & (Lay::kGran - 1))) +
                                8 * h32);
-        // (the intermediate's 2^-8 is a power of two: folded into the factor, it rounds the same)
+        // (the intermediate's 2^-4 is a power of two: folded into the factor, it rounds the same)
         const float fs = EPI == kEpiPartial ? f * kPartialScale : f;
         f32x2 y[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) y[u] = f32x2{o[t][4 * a + 2 * u] * fs, o[t][4 * a + 2 * u + 1] * fs};
         uint32_t w[2];
         if constexpr (EPI == kEpiPartial) {
-          // the gated intermediate: fp16 of y * 2^-8, one packed conversion per pair
+          // the gated intermediate: fp16 of y * 2^-4, one packed conversion per pair
 #pragma unroll
           for (int u = 0; u < 2; ++u)
             w[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y[u], f16x2));

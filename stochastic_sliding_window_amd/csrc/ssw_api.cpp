@@ -169,7 +169,7 @@ static int run_gated(const char* who, const void* q, const void* k, const void* 
   const float* g_sa = gates;
   const float* g_swa = gates + (size_t)B * n * Hq;
   // Pass 1: the SA pass leaves g_sa * Y_sa in `out` as the intermediate, at the scattered rows
-  // sigma[p] (fp32, or for bf16 outputs fp16 bits of the value times 2^-8, so that the sum is
+  // sigma[p] (fp32, or for bf16 outputs fp16 bits of the value times 2^-4, so that the sum is
   // in effect rounded to bf16 once).  sigma being a bijection means every row is written once.
   ssw::BandLaunch a1 =
       make_launch(q, k, v, sigma, window, causal, g_sa, out, B, n, Hq, Hkv, d, dtype);

@@ -365,6 +365,32 @@ def test_sa_alone_build_switch(w, causal):
     _say(f"SA alone w={w} causal={causal}: max err {err:.3e}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("vscale", [1e-3, 1e3])
+def test_gated_intermediate_across_magnitudes(vscale, causal):
+    """The bf16 gated layer keeps g_sa Y_sa between its passes as fp16 of the value times 2^-4:
+    normal fp16 for 2^-10 <= |g_sa Y_sa| < 1.05e6, a fixed 2^-20 step below.  V scaled by 1e-3
+    puts the outputs around 1e-4, partly below that normal range; V scaled by 1e3 puts them
+    around 1e2.  bf16 rounding is relative, so the unit-scale bar is carried to the output's
+    scale: max |err| <= 1.5e-2 * max |oracle| (about 1e-5 at the small scale, where a 2^-16 step
+    would already use most of it).  Every row."""
+    B, n, Hq, Hkv, d, w = 1, 1024, 8, 2, 128, 64
+    q, k, v = synth.qkv(71, B, n, Hq, Hkv, d, "bf16")
+    g = synth.gates(71, B, n, Hq)
+    v = (v.float() * vscale).to(torch.bfloat16)
+    sig_dev, sig = _sigma(72, n)
+    out = ssw.gated_sa_swa_forward(q.to(DEV), k.to(DEV), v.to(DEV), sig_dev, w, causal, g.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.gated_forward(q, k, v, sig, w, causal, g)
+    got = out.float().cpu().numpy().astype(np.float64)
+    scale = float(np.abs(ref).max())
+    err = float(np.abs(got - ref).max())
+    _say(f"gated, V x {vscale:g}, causal={causal}: max |oracle| {scale:.3e}, max err {err:.3e} "
+         f"({err / scale:.2e} of it)")
+    assert np.isfinite(got).all()
+    assert err <= 1.5e-2 * scale, (err, scale)
+
+
 @pytest.mark.parametrize("w", [448, 449])
 def test_gated_d64_build_switch(w):
     """The gated layer's SA pass at d = 64 also has a three-waves-per-SIMD build, used when a
