@@ -65,9 +65,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    # untimed steps before the timed region: in a fresh process the first few dozen steps run
-    # several per cent slower than the steady state (measured: 10 warm-up steps gave 481 us per
-    # step, 60 gave 460 us), so the default reaches the steady state first (about 25 ms)
+    # untimed steps before the timed region: the shader clock moves over the first few dozen
+    # steps of a fresh process (measured on one box: 518 us per step over 20 steps after 5
+    # warm-up steps, 436 us over 100 steps after 50), so the default reaches the steady state
+    # first (about 25 ms)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--window", type=int, default=128)
     ap.add_argument("--sweep", action="store_true", help="also time SA / SWA alone at w 16 .. 512")
