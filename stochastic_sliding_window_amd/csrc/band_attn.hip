@@ -33,9 +33,9 @@
 //   * Epilogue: divide by the row sum, multiply by the gate, scatter to row sigma[p] (the gated
 //     layer's SA pass stores its fp16 intermediate there; its SWA pass adds to it).
 //   * Two builds of the sigma-gathered kernel (template flag W3): two waves per SIMD with a
-//     4-slot ring and two chunks per loop step, and (bf16) three waves per SIMD with a 3-slot
-//     ring and one chunk per step; the dispatcher picks the latter when a workgroup's band fits
-//     its sigma segment.
+//     4-slot ring and two chunks per loop step, and (bf16) three waves per SIMD at d = 128 (four
+//     at d = 64) with a 3-slot ring and one chunk per step; the dispatcher picks the latter when a
+//     workgroup's band fits its sigma segment.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -70,18 +70,19 @@ constexpr int kChunk = 32;
 //   * two waves per SIMD (register allocation sized for it), a 4-stage ring (kStages - 1 chunks
 //     in flight) consumed two 32-key chunks per loop step (bf16; fp32 computes the scores of
 //     chunk c + 1 alongside the softmax of chunk c), and a 2048-entry sigma segment;
-//   * bf16 only, three waves per SIMD: a 3-stage ring, one chunk per step and a 1024-entry sigma
-//     segment (3 x 16 KB + 4 KB of LDS per workgroup at d = 128, so three workgroups fit a CU).
-//     The dispatcher launches it when a workgroup's band fits one segment; longer bands use the
-//     two-wave build.  At d = 128 the causal build recomputes the K/V LDS offsets at their use
-//     from one base register each and reads sigma for the mask in two halves, to fit the
-//     registers of three waves.
+//   * bf16 only, three waves per SIMD at d = 128 and four at d = 64: a 3-stage ring, one chunk per
+//     step and a 1024-entry sigma segment (3 x 16 KB + 4 KB of LDS per workgroup at d = 128, so
+//     three workgroups fit a CU; 28 KB at d = 64, four workgroups).  The dispatcher launches it
+//     when a workgroup's band fits one segment; longer bands use the two-wave build.  The causal
+//     build recomputes the K/V LDS offsets at their use from one base register each and reads
+//     sigma for the mask in two halves, to fit the registers of three (d = 128: 168) or four
+//     (d = 64: 128) waves.
 // The identity-sigma (SWA) kernels hold no sigma in LDS and fewer registers, so they run at three
 // waves per SIMD with a 3-stage ring and one chunk per step.
 constexpr int kStages = 4;
 constexpr int kWavesPerSimd = 2;
 constexpr int kSigCap = 2048;      // sigma entries held in LDS at a time (two-wave build)
-constexpr int kSigCapW3 = 1024;    // the same, three-waves build
+constexpr int kSigCapW3 = 1024;    // the same, W3 build
 constexpr int kWavesPerSimdSwa = 3;
 constexpr int kStagesSwa = 3;
 constexpr float kLazy = 8.0f;  // reference max may lag the true max by up to 2^8 (log2 units)
@@ -260,25 +261,26 @@ __device__ __forceinline__ int xcd_local_order(int i, int nblocks) {
 
 template <typename T, bool PERM, int EPI, bool W3>
 constexpr bool kIsW3 = W3 && PERM && sizeof(T) == 2;
-template <typename T, bool PERM, int EPI, bool W3>
-constexpr int kWavesPerEU =
-    kIsW3<T, PERM, EPI, W3> ? 3 : (PERM || sizeof(T) != 2) ? kWavesPerSimd : kWavesPerSimdSwa;
+template <typename T, bool PERM, int EPI, bool W3, int D>
+constexpr int kWavesPerEU = kIsW3<T, PERM, EPI, W3>       ? (D == 64 ? 4 : 3)
+                            : (PERM || sizeof(T) != 2) ? kWavesPerSimd
+                                                       : kWavesPerSimdSwa;
 
 template <typename T, int D, bool PERM, bool SIGMASK, int EPI, bool W3>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kWavesPerEU<T, PERM, EPI, W3>,
-                                   kWavesPerEU<T, PERM, EPI, W3>)))
+__attribute__((amdgpu_waves_per_eu(kWavesPerEU<T, PERM, EPI, W3, D>,
+                                   kWavesPerEU<T, PERM, EPI, W3, D>)))
 void band_attn_kernel(Params prm) {
   constexpr bool kW3 = kIsW3<T, PERM, EPI, W3>;
   using Lay = Layout<T, D, PERM, kW3>;
   constexpr int kSegChunks = Lay::kSegChunks;  // chunks per sigma segment
   constexpr bool kPipe = !kW3 && PERM;  // scores of chunk c + 1 beside the softmax of chunk c
   constexpr bool kBf16 = Lay::kBf16;
-  // At three waves per SIMD (168 registers) the causal sigma-gathered kernel at d = 128
-  // recomputes the K/V LDS offsets at their use (from one base register each) instead of holding
-  // them across the loop, and reads sigma for the causal mask in two halves.  (d = 64 fits
-  // without.)
-  constexpr bool kLeanAny = kW3 && SIGMASK && D == 128;
+  // At three waves per SIMD (d = 128: 168 registers) or four (d = 64: 128) the causal
+  // sigma-gathered kernel recomputes the K/V LDS offsets at their use (from one base register
+  // each) instead of holding them across the loop, and reads sigma for the causal mask in two
+  // halves.  (Held offsets spilled 11 registers at d = 64 and four waves.)
+  constexpr bool kLeanAny = kW3 && SIGMASK;
   constexpr bool kLean = kLeanAny;  // K/V LDS offsets
   constexpr bool kLeanMask = kLeanAny;
   __shared__ __attribute__((aligned(16))) char smem[Lay::kSmem];
@@ -1311,8 +1313,8 @@ static hipError_t launch_d(const BandLaunch& a, const Params& prm, hipStream_t s
   // SWA pass second, which adds to it (kEpiAddPartial); everything else stores plainly.
   if (a.perm) {
     const bool part = a.epilogue == kEpiPartial;
-    // The three-waves-per-SIMD build (bf16) when a workgroup's band, at most ceil(kColsWG / G)
-    // + 1 slots plus L + R keys, fits its 1024-entry sigma segment.
+    // The W3 build (bf16; three or four waves per SIMD) when a workgroup's band, at most
+    // ceil(kColsWG / G) + 1 slots plus L + R keys, fits its 1024-entry sigma segment.
     const int64_t band = (kColsWG + prm.G - 1) / prm.G + 1 + (int64_t)prm.L + prm.R;
     if constexpr (sizeof(T) == 2) {
       if (band <= kSigCapW3) {

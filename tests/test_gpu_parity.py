@@ -393,10 +393,10 @@ def test_gated_intermediate_across_magnitudes(vscale, causal):
 
 @pytest.mark.parametrize("w", [448, 449])
 def test_gated_d64_build_switch(w):
-    """The gated layer's SA pass at d = 64 also has a three-waves-per-SIMD build, used when a
-    workgroup's band fits its 1024-entry sigma segment; with one query head per KV head (G = 1)
-    the switch lies between w = 448 and w = 449.  Both sides of the gated layer against the oracle
-    on sampled rows, bf16 bar."""
+    """The gated layer's SA pass at d = 64 also has the build with more waves per SIMD (four at
+    d = 64), used when a workgroup's band fits its 1024-entry sigma segment; with one query head
+    per KV head (G = 1) the switch lies between w = 448 and w = 449.  Both sides of the gated
+    layer against the oracle on sampled rows, bf16 bar."""
     B, n, Hq, Hkv, d = 2, 1536, 2, 2, 64
     host, dev = _data(51, B, n, Hq, Hkv, d, "bf16")
     sig_dev, sig = _sigma(52, n)
