@@ -78,7 +78,8 @@ constexpr int kChunk = 32;
 //     sigma for the mask in two halves, to fit the registers of three (d = 128: 168) or four
 //     (d = 64: 128) waves.
 // The identity-sigma (SWA) kernels hold no sigma in LDS and fewer registers, so they run at three
-// waves per SIMD with a 3-stage ring and one chunk per step.
+// waves per SIMD (four at d = 64, which takes 106 registers) with a 3-stage ring and one chunk
+// per step.
 constexpr int kStages = 4;
 constexpr int kWavesPerSimd = 2;
 constexpr int kSigCap = 2048;      // sigma entries held in LDS at a time (two-wave build)
@@ -264,6 +265,7 @@ constexpr bool kIsW3 = W3 && PERM && sizeof(T) == 2;
 template <typename T, bool PERM, int EPI, bool W3, int D>
 constexpr int kWavesPerEU = kIsW3<T, PERM, EPI, W3>       ? (D == 64 ? 4 : 3)
                             : (PERM || sizeof(T) != 2) ? kWavesPerSimd
+                            : D == 64                  ? 4
                                                        : kWavesPerSimdSwa;
 
 template <typename T, int D, bool PERM, bool SIGMASK, int EPI, bool W3>
