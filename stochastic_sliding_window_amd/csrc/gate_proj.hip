@@ -10,11 +10,13 @@
 // Mapping onto the chip: a skinny GEMM (N = 2 Hq <= 128 columns, K = Hm) bound by reading x.  A
 // workgroup takes 128 rows, a wave 32 of them; each wave accumulates its 32 x N tile with bf16
 // 32x32x16 MFMAs.  Its x rows are read row-contiguously in blocks of 64 k, one block ahead, and
-// staged through a wave-private LDS buffer into the A-operand layout; the projection's rows
-// w_t[j] (B operands; w_t is [N, Hm] row-major, the usual layout of a linear layer's weight) are
-// read straight from memory (they stay in the L2).  A split of the k range over the waves of a
-// workgroup (4x the waves in flight) measured slower: every workgroup then reads all of w_t.  The epilogue adds the bias, applies the sigmoid and scatters the columns to their
-// gate plane.
+// staged through a wave-private LDS buffer into the A-operand layout.  The matching block of the
+// projection's rows w_t[j] (B operands; w_t is [N, Hm] row-major, the usual layout of a linear
+// layer's weight) is read row-contiguously by the whole workgroup into a shared, double-buffered
+// LDS block, so that w_t crosses the L2 once per workgroup, in whole rows.  A split of the k
+// range over the waves of a workgroup (4x the waves in flight) measured slower: every workgroup
+// then reads all of w_t once per wave.  The epilogue adds the bias, applies the sigmoid and
+// scatters the columns to their gate plane.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,6 +33,7 @@ constexpr int kThreads = 256;
 constexpr int kRowsWG = 128;
 constexpr int kMaxTiles = 4;  // N <= 128
 constexpr int kUnroll = 4;    // k steps of 16 per loop iteration
+constexpr int kSub = 2;       // 64-k sub-blocks per barrier (of the shared w_t buffer)
 
 struct Params {
   const char* x;
@@ -40,16 +43,27 @@ struct Params {
   int rows, Hm, Hq, N;
 };
 
+// Granule g of a 128-byte LDS row r sits at granule position g ^ swz(r).  A 16-byte read by 16
+// lanes touching rows r0 .. r0 + 15 (one granule each) then covers all 64 banks: odd and even rows
+// take the two halves of the banks, and the eight rows of each half get eight distinct positions.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
 template <int NT>
 __global__ __launch_bounds__(kThreads) void gate_proj_kernel(Params prm) {
-  __shared__ __attribute__((aligned(16))) char x_lds[4][32 * 128];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) char x_lds[4][kSub][32 * 128];
+  // the workgroup's block of w_t (NT * 32 rows x 64 k per sub-block), double-buffered and shared
+  // by the waves
+  __shared__ __attribute__((aligned(16))) char w_lds[2][kSub][NT * 32 * 128];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int r32 = lane & 31;
   const int h32 = lane >> 5;
   const int row0 = blockIdx.x * kRowsWG + wave * 32;
-  if (row0 >= prm.rows) return;  // wave-uniform: no barrier in this kernel
-  const int myrow = min(row0 + r32, prm.rows - 1);
+  // waves past the last row take part in the shared loads and barriers only
+  const bool wave_on = row0 < prm.rows;
+  const int row0c = wave_on ? row0 : prm.rows - 1;
+  const int myrow = min(row0c + r32, prm.rows - 1);
   const int64_t rb = (int64_t)prm.Hm * 2;
   const char* xrow = prm.x + (int64_t)myrow * rb + 16 * h32;
   const char* wrow[NT];
@@ -67,47 +81,95 @@ __global__ __launch_bounds__(kThreads) void gate_proj_kernel(Params prm) {
   // holds column 32t + r32 at the same k
   const int steps = prm.Hm / 16;
   int s = 0;
-  // Blocks of 64 k: the wave's 32 x rows are read row-contiguously (8 lanes cover a row's
-  // 128 bytes), one block ahead in registers, and go through a wave-private LDS buffer (granules
-  // XOR-swizzled by row) from which the A operands are read.
+  // Blocks of kSub * 64 k, one barrier each.  The wave's 32 x rows are read row-contiguously
+  // (8 lanes cover 128 bytes of a row), one block ahead in registers, and go through a
+  // wave-private LDS buffer.  The block of w_t (all N rows) is read row-contiguously by the whole
+  // workgroup, one block ahead, into a shared double buffer: every wave of the workgroup takes its
+  // B operands from it, so w_t crosses the L2 once per workgroup instead of once per wave, and in
+  // whole rows.
   {
-    char* xl = x_lds[wave];
-    const int nblk = prm.Hm / 64;
-    const char* xwave = prm.x + (int64_t)row0 * rb;
-    auto load_blk = [&](int kb, u32x4 (&r)[4]) {
+    const int nblk = prm.Hm / (64 * kSub);
+    const char* xwave = prm.x + (int64_t)row0c * rb;
+    auto load_x = [&](int kb, u32x4 (&r)[kSub][4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = min(8 * i + lane / 8, prm.rows - 1 - row0);
-        r[i] = *(const u32x4*)(xwave + (int64_t)row * rb + kb * 128 + (lane % 8) * 16);
-      }
+      for (int h = 0; h < kSub; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = min(8 * i + lane / 8, prm.rows - 1 - row0c);
+          r[h][i] = *(const u32x4*)(xwave + (int64_t)row * rb + (kSub * kb + h) * 128 +
+                                    (lane % 8) * 16);
+        }
     };
-    u32x4 cur[4], nxt[4];
-    if (nblk > 0) load_blk(0, cur);
-    for (int kb = 0; kb < nblk; ++kb) {
-      if (kb + 1 < nblk) load_blk(kb + 1, nxt);
+    // thread tid brings granule tid % 8 of w_t rows 32 i + tid / 8
+    auto load_w = [&](int kb, u32x4 (&r)[kSub][NT]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 8 * i + lane / 8;
-        *(u32x4*)(xl + row * 128 + ((((lane % 8) ^ (row & 7))) << 4)) = cur[i];
-      }
-      // the wave's own LDS stores precede its reads (in-order LDS queue); nothing else shares
-      // this buffer
+      for (int h = 0; h < kSub; ++h)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const u32x4 a = *(const u32x4*)(xl + r32 * 128 + (((2 * u + h32) ^ (r32 & 7)) << 4));
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, a),
-              __builtin_bit_cast(bf16x8, *(const u32x4*)(wrow[t] + 32 * (4 * kb + u))), acc[t],
-              0, 0, 0);
-      }
-      if (kb + 1 < nblk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+        for (int i = 0; i < NT; ++i) {
+          const int row = min(32 * i + tid / 8, prm.N - 1);
+          r[h][i] = *(const u32x4*)(prm.w_t + (int64_t)row * rb + (kSub * kb + h) * 128 +
+                                    (tid % 8) * 16);
+        }
+    };
+    u32x4 xc[kSub][4], xn[kSub][4], wc[kSub][NT], wn[kSub][NT];
+    if (nblk > 0) {
+      load_x(0, xc);
+      load_w(0, wc);
     }
-    s = 4 * nblk;
+    for (int kb = 0; kb < nblk; ++kb) {
+#pragma unroll
+      for (int h = 0; h < kSub; ++h) {
+        char* wl = w_lds[kb & 1][h];
+        char* xl = x_lds[wave][h];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          const int row = 32 * i + tid / 8;
+          *(u32x4*)(wl + row * 128 + (((tid % 8) ^ swz(row)) << 4)) = wc[h][i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 8 * i + lane / 8;
+          *(u32x4*)(xl + row * 128 + (((lane % 8) ^ swz(row)) << 4)) = xc[h][i];
+        }
+      }
+      // block kb of w_t is in place for every wave; every wave is done with block kb - 2, whose
+      // buffer was just refilled (its reads came before the previous barrier)
+      __syncthreads();
+      if (kb + 1 < nblk) {
+        load_x(kb + 1, xn);
+        load_w(kb + 1, wn);
+      }
+      if (wave_on) {
+#pragma unroll
+        for (int h = 0; h < kSub; ++h) {
+          const char* wl = w_lds[kb & 1][h];
+          const char* xl = x_lds[wave][h];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int gpos = ((2 * u + h32) ^ swz(r32)) << 4;
+            const u32x4 a = *(const u32x4*)(xl + r32 * 128 + gpos);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, a),
+                  __builtin_bit_cast(bf16x8, *(const u32x4*)(wl + (32 * t + r32) * 128 + gpos)),
+                  acc[t], 0, 0, 0);
+          }
+        }
+      }
+      if (kb + 1 < nblk) {
+#pragma unroll
+        for (int h = 0; h < kSub; ++h) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xc[h][i] = xn[h][i];
+#pragma unroll
+          for (int i = 0; i < NT; ++i) wc[h][i] = wn[h][i];
+        }
+      }
+    }
+    s = 4 * kSub * nblk;
   }
+  if (!wave_on) return;  // the remaining steps have no barrier
   for (; s + kUnroll <= steps; s += kUnroll) {
     u32x4 a[kUnroll], bw[kUnroll][NT];
 #pragma unroll
