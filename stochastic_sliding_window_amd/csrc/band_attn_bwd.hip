@@ -19,8 +19,8 @@
 //     transposed LDS reads, with dS^T already in B-operand order.
 //   * bwd_dkdv_kernel is key-major: a wave owns 32 key slots of one KV head (their K rows are B
 //     operands in registers, their V rows sit in LDS), the workgroup 128.  Its loop streams
-//     chunks of 32 query columns (Q and dy rows plus each column's log-sum-exp, Delta, gate,
-//     slot and original index): S = Q K^T and dP = dy V^T leave P and dS with one key per lane,
+//     chunks of 32 query columns (Q and dy rows plus each column's log-sum-exp, Delta, gate and
+//     original index): S = Q K^T and dP = dy V^T leave P and dS with one key per lane,
 //     which is the B operand of dV^T += (dy)^T (g P) and dK^T += Q^T dS.
 //   * Chunks are gathered through sigma by direct buffer-to-LDS loads into an LDS ring (three
 //     chunks ahead in the dQ kernel, one in the dK/dV kernel).  Rows sit in MFMA row order, their
@@ -495,10 +495,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void bwd_dkdv_kernel(Params prm) {
   using LY = Lay<D>;
   // per stage: Q rows, dy rows, then per column lse, Delta, gate (64 floats each: a 4-byte DMA
-  // covers 64 lanes), then 64 ints whose upper 32 hold the columns' original indices
+  // covers 64 lanes), then the columns' original indices (32 ints)
   constexpr int kMetaOff = 2 * LY::kMat;
-  constexpr int kStage = kMetaOff + 3 * 64 * 4 + 2 * kChunk * 4;
-  constexpr int kSlotOff = kMetaOff + 3 * 64 * 4;
+  constexpr int kOrigOff = kMetaOff + 3 * 64 * 4;
+  constexpr int kStage = kOrigOff + kChunk * 4;
   constexpr int kRowsPerDma = 1024 / LY::kRowBytes;
   constexpr int kDmaMat = LY::kMat / 1024;  // DMA instructions per matrix and chunk
   constexpr int kDW = 2 * kDmaMat / 4;      // per wave
@@ -567,8 +567,8 @@ void bwd_dkdv_kernel(Params prm) {
   auto orig_of_slot = [&](int slot) { return PERM ? sig_lds[slot - seg_s0] : slot; };
 
   // ---- chunk staging: direct buffer-to-LDS loads of the chunk's Q and dy rows (MFMA row order,
-  // granules XOR-swizzled by row) and of its columns' lse, Delta and gate; the slot and original
-  // index of each column are written by the first 32 threads.  One chunk is in flight while the
+  // granules swizzled by row) and of its columns' lse, Delta and gate; the original index of each
+  // column is written by the first 32 threads (causal mode).  One chunk is in flight while the
   // previous one is scored (two stages: the V rows of the tile take the rest of the LDS).
   const uint32_t smem_lds = lds_dma::lds_addr(smem);
   const int64_t qd_batch = (int64_t)b * n * prm.Hq;
@@ -614,9 +614,9 @@ void bwd_dkdv_kernel(Params prm) {
       lds_dma::load4(rs_m, st_lds + kMetaOff + wave * 256, moff);
     }
     if (SIGMASK && tid < kChunk) {
-      int* mi = (int*)(smem + (c & 1) * kStage + kSlotOff);
+      int* mi = (int*)(smem + (c & 1) * kStage + kOrigOff);
       // the column's token, its original index (columns past the end fail the band test)
-      mi[kChunk + tid] = c0 + tid < nG ? orig_of_slot(slot0 + div_small(rem0 + tid, prm.inv_g)) : -1;
+      mi[tid] = c0 + tid < nG ? orig_of_slot(slot0 + div_small(rem0 + tid, prm.inv_g)) : -1;
     }
   };
 
@@ -678,7 +678,7 @@ void bwd_dkdv_kernel(Params prm) {
       t_off[db][1] = tb1 ^ (db << 6);
     }
     const float* mf = (const float*)(Qst + kMetaOff);  // lse [0, 64), Delta [64, ..), gate
-    const int* mi = (const int*)(Qst + kSlotOff);        // original index at [32, 64)
+    const int* mi = (const int*)(Qst + kOrigOff);        // original index of each column
 
     // S[col][key] = <Q, K>, dP[col][key] = <dy, V>; output register i of lane half h32 holds
     // column 16(i / 8) + 8h32 + i % 8 of the chunk, for the lane's key
@@ -708,7 +708,7 @@ void bwd_dkdv_kernel(Params prm) {
       const f32x4 del4 = *(const f32x4*)(mq + 64 * 4);
       const f32x4 gt4 = *(const f32x4*)(mq + 128 * 4);
       u32x4 or4 = {0, 0, 0, 0};
-      if constexpr (SIGMASK) or4 = *(const u32x4*)((const char*)mi + kChunk * 4 + moff + 4 * e0);
+      if constexpr (SIGMASK) or4 = *(const u32x4*)((const char*)mi + moff + 4 * e0);
       float last = 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
