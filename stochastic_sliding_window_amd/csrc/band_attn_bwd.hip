@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "band_attn.h"
 #include "lds_dma.h"
@@ -440,24 +441,34 @@ void bwd_dq_kernel(Params prm) {
       const int kc0 = kbeg + c * kChunk;
       // dS of the lane's 16 scores, four keys at a time (registers 4qd .. 4qd + 3 hold keys
       // e0 .. e0 + 3): their sigma arrives as one 16-byte read and the mask is a select (exp2
-      // runs for masked scores too), so that no element waits on an LDS read of its own.
+      // runs for masked scores too), so that no element waits on an LDS read of its own.  In an
+      // interior chunk (every key inside the band of every slot of the wave, and before the
+      // sequence end) only the causal test remains.
       bf16x8 dsb[2];
+      auto scores = [&](auto interior_c) {
+        constexpr bool kInterior = decltype(interior_c)::value;
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int e0 = 16 * (qd >> 1) + 8 * h32 + 4 * (qd & 1);
-        u32x4 sg4 = {0, 0, 0, 0};
-        if constexpr (SIGMASK) sg4 = *(const u32x4*)(sig_lds + (kc0 + e0 - seg_key0));
+        for (int qd = 0; qd < 4; ++qd) {
+          const int e0 = 16 * (qd >> 1) + 8 * h32 + 4 * (qd & 1);
+          u32x4 sg4 = {0, 0, 0, 0};
+          if constexpr (SIGMASK) sg4 = *(const u32x4*)(sig_lds + (kc0 + e0 - seg_key0));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * qd + u;
-          const int key = kc0 + e0 + u;
-          bool ok = (key >= myslot - L) & (key <= myslot + R) & (key < n);
-          if constexpr (SIGMASK) ok = ok & ((int)sg4[u] <= myorig);
-          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -lse2));
-          const float p = ok ? x : 0.f;
-          dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gate_v, dp[r], -delta));
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * qd + u;
+            const int key = kc0 + e0 + u;
+            bool ok = true;
+            if constexpr (!kInterior) ok = (key >= myslot - L) & (key <= myslot + R) & (key < n);
+            if constexpr (SIGMASK) ok = ok & ((int)sg4[u] <= myorig);
+            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -lse2));
+            const float p = ok ? x : 0.f;
+            dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gate_v, dp[r], -delta));
+          }
         }
-      }
+      };
+      if (kc0 >= w_shi - L && kc0 + kChunk - 1 <= w_slo + R && kc0 + kChunk - 1 < n)
+        scores(std::true_type{});
+      else
+        scores(std::false_type{});
       // dQ^T[d][col] += K^T[d][key] dS^T[key][col]
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -635,6 +646,9 @@ void bwd_dkdv_kernel(Params prm) {
   // i.e. band_lo <= x <= band_hi.
   const int band_lo = (myk - R) * G - col_lo;
   const int band_hi = min(myk + L + 1, n) * G - 1 - col_lo;
+  // the columns inside the band of every key of the wave
+  const int wband_lo = __builtin_amdgcn_readfirstlane((wk_hi - R) * G - col_lo);
+  const int wband_hi = __builtin_amdgcn_readfirstlane(min(wk_lo + L + 1, n) * G - 1 - col_lo);
   // Without a gate the stages' gate entries hold 1 (the gate DMA never writes them).
   if (!prm.gate && tid < 2 * kChunk)
     *(float*)(smem + (tid / kChunk) * kStage + kMetaOff + 128 * 4 + (tid % kChunk) * 4) = 1.0f;
@@ -696,35 +710,45 @@ void bwd_dkdv_kernel(Params prm) {
     // runs for masked scores too), so that no score waits on an LDS read of its own.  Each
     // group's reads are issued after the previous group's results (an empty asm ties their
     // address to them): all sixteen scores' values at once would not fit in the registers.
+    // In an interior chunk (every column inside the band of every key of the wave) only the
+    // causal test remains.
     const int lo = band_lo - c * kChunk - 8 * h32;
     const int hi = band_hi - c * kChunk - 8 * h32;
-    int moff = 32 * h32;  // byte offset of the lane half's first column in each metadata array
     bf16x8 pb[2], dsb[2];
+    auto scores = [&](auto interior_c) {
+      constexpr bool kInterior = decltype(interior_c)::value;
+      int moff = 32 * h32;  // byte offset of the lane half's first column in each metadata array
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int e0 = 16 * (qd >> 1) + 4 * (qd & 1);
-      const char* mq = (const char*)mf + moff + 4 * e0;
-      const f32x4 lse4 = *(const f32x4*)(mq);
-      const f32x4 del4 = *(const f32x4*)(mq + 64 * 4);
-      const f32x4 gt4 = *(const f32x4*)(mq + 128 * 4);
-      u32x4 or4 = {0, 0, 0, 0};
-      if constexpr (SIGMASK) or4 = *(const u32x4*)((const char*)mi + moff + 4 * e0);
-      float last = 0.f;
+      for (int qd = 0; qd < 4; ++qd) {
+        const int e0 = 16 * (qd >> 1) + 4 * (qd & 1);
+        const char* mq = (const char*)mf + moff + 4 * e0;
+        const f32x4 lse4 = *(const f32x4*)(mq);
+        const f32x4 del4 = *(const f32x4*)(mq + 64 * 4);
+        const f32x4 gt4 = *(const f32x4*)(mq + 128 * 4);
+        u32x4 or4 = {0, 0, 0, 0};
+        if constexpr (SIGMASK) or4 = *(const u32x4*)((const char*)mi + moff + 4 * e0);
+        float last = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * qd + u;
-        bool ok = (e0 + u >= lo) & (e0 + u <= hi);
-        if constexpr (SIGMASK) ok = ok & (ktok <= (int)or4[u]);
-        const float x =
-            __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -lse4[u] * kLog2e));
-        const float p = ok ? x : 0.f;
-        const float pg = p * gt4[u];
-        pb[r >> 3][r & 7] = (__bf16)pg;
-        dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gt4[u], dp[r], -del4[u]));
-        last = pg;
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * qd + u;
+          bool ok = true;
+          if constexpr (!kInterior) ok = (e0 + u >= lo) & (e0 + u <= hi);
+          if constexpr (SIGMASK) ok = ok & (ktok <= (int)or4[u]);
+          const float x =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], prm.scale_log2, -lse4[u] * kLog2e));
+          const float p = ok ? x : 0.f;
+          const float pg = p * gt4[u];
+          pb[r >> 3][r & 7] = (__bf16)pg;
+          dsb[r >> 3][r & 7] = (__bf16)(p * __builtin_fmaf(gt4[u], dp[r], -del4[u]));
+          last = pg;
+        }
+        asm volatile("" : "+v"(moff) : "v"(last));
       }
-      asm volatile("" : "+v"(moff) : "v"(last));
-    }
+    };
+    if (c * kChunk >= wband_lo && c * kChunk + kChunk - 1 <= wband_hi)
+      scores(std::true_type{});
+    else
+      scores(std::false_type{});
     // dV^T[d][key] += dy^T[d][col] (g P)[col][key];  dK^T[d][key] += Q^T[d][col] dS[col][key]
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
