@@ -125,6 +125,9 @@ SHAPES = [
     (1, 513, 16, 2, 128, 100),
     (2, 300, 6, 2, 64, 17),
     (1, 2100, 4, 1, 128, 128),
+    (1, 300, 16, 1, 128, 33),   # G = 16: a 128-column tile is 8 slots
+    (1, 600, 32, 1, 64, 50),    # G = 32: 4 slots per tile
+    (1, 200, 64, 1, 64, 20),    # G = 64: 2 slots per tile, a slot's heads split over two waves
 ]
 
 
