@@ -77,13 +77,14 @@ def _fwd_tol(ref):
     return 1.5e-2 + np.maximum(0.0, half_spacing - 2.0 ** -7)
 
 
-# (B, n, Hq, Hkv, d, w): several workgroup tiles and ragged tails; GQA group sizes 1, 2, 3, 4, 8
+# (B, n, Hq, Hkv, d, w): several workgroup tiles and ragged tails; GQA group sizes 1, 2, 3, 4, 8, 32
 SHAPES = [
     (1, 300, 8, 2, 128, 16),
     (2, 517, 4, 4, 64, 40),
     (1, 200, 12, 4, 128, 7),
     (1, 389, 8, 2, 64, 33),
     (1, 130, 8, 1, 128, 130),   # window covers the sequence
+    (1, 300, 32, 1, 64, 24),    # G = 32: a query-column tile is 4 slots
 ]
 
 
