@@ -548,11 +548,27 @@ void bwd_dkdv_kernel(Params prm) {
   const int khi_wg = min(K0 + kTile - 1, n - 1);
   const int col_lo = max(0, K0 - R) * G;
   const int col_hi = min(n - 1, khi_wg + L) * G + G - 1;
-  const int nchunks = (col_hi - col_lo) / kChunk + 1;
+  // chunks lie on one grid of kChunk columns for every workgroup: chunk c holds the columns
+  // col_base + c kChunk + [0, kChunk)
+  const int col_base = col_lo / kChunk * kChunk;
+  const int nchunks = (col_hi - col_base) / kChunk + 1;
   const int wk_lo = min(kw0, n - 1);
   const int wk_hi = min(kw0 + 31, n - 1);
-  const int c_first = (max(0, wk_lo - R) * G - col_lo) / kChunk;
-  const int c_last = (min(n - 1, wk_hi + L) * G + G - 1 - col_lo) / kChunk;
+  const int c_first = (max(0, wk_lo - R) * G - col_base) / kChunk;
+  const int c_last = (min(n - 1, wk_hi + L) * G + G - 1 - col_base) / kChunk;
+  // Visiting order.  About three neighbouring workgroups read each chunk, and in band order they
+  // would reach it many chunks apart, after the L2 has cycled.  So, when the sigma of every slot
+  // the chunks touch fits one LDS segment, step i takes the chunk whose index on the common grid
+  // is i modulo nchunks: workgroups of equal chunk counts that start together read each chunk
+  // at the same step.  Otherwise the chunks go in band order and the segment moves along.
+  const int last_slot_all = min(n - 1, (col_base + nchunks * kChunk - 1) / G);
+  const bool one_seg = !PERM || last_slot_all - col_base / G < kSigCap;
+  const int a0 = col_base / kChunk;
+  const int rot = one_seg ? (nchunks - a0 % nchunks) % nchunks : 0;
+  auto chunk_at = [&](int i) {
+    const int c = i + rot;
+    return c >= nchunks ? c - nchunks : c;
+  };
 
   // ---- K row of the lane's key as B operands (k step kb holds d = 16kb + 8h32 + [0, 8)); its V
   // row goes to LDS in the same swizzled layout as the stage matrices (row = key within the tile)
@@ -568,7 +584,7 @@ void bwd_dkdv_kernel(Params prm) {
   }
 
   // ---- sigma of the query slots [seg_s0, seg_s0 + kSigCap), in LDS (permuted operator)
-  int seg_s0 = col_lo / G;
+  int seg_s0 = col_base / G;
   auto load_sigma_seg = [&](int s0) {
     for (int i = tid; i < kSigCap; i += kThreads) {
       const int slot = s0 + i;
@@ -592,42 +608,54 @@ void bwd_dkdv_kernel(Params prm) {
                 : wave == 1 ? (const void*)(prm.delta + qd_batch)
                             : (const void*)(prm.gate ? prm.gate + qd_batch : prm.lse + qd_batch),
       m_range);
-  // row of column c0 + e within batch row b: token row * Hq + query head
-  auto col_row = [&](int slot0, int rem0, int e, int& slot) {
-    const int x = rem0 + e;
-    const int ds = div_small(x, prm.inv_g);
-    slot = slot0 + ds;
-    return orig_of_slot(slot) * prm.Hq + g * G + (x - ds * G);
-  };
-  auto dma_chunk = [&](int c) {
-    const int c0 = col_lo + c * kChunk;
+  auto dma_chunk = [&](int c, int stage) {
+    const int c0 = col_base + c * kChunk;
     const int slot0 = c0 / G;  // wave-uniform
     const int rem0 = c0 - slot0 * G;
-    const uint32_t st_lds = smem_lds + (uint32_t)((c & 1) * kStage);
+    const uint32_t st_lds = smem_lds + (uint32_t)(stage * kStage);
+    // Lane l finds the row of chunk entry l % 32 once (its slot, the slot's token, the query
+    // head), and each row DMA takes the rows it needs from those lanes by ds_bpermute.  The lane
+    // index is an opaque copy, so the lane constants below are recomputed per chunk rather than
+    // held across the loop beside the accumulators.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int e_l = ln & (kChunk - 1);
+    const bool ok_l = c0 + e_l < nG;  // columns past the end read as zeros; their band test fails
+    const int x = rem0 + (ok_l ? e_l : nG - 1 - c0);
+    const int ds = div_small(x, prm.inv_g);
+    const int orig_l = orig_of_slot(slot0 + ds);
+    const int row_l = orig_l * prm.Hq + g * G + (x - ds * G);  // token row * Hq + query head
+    const uint32_t rb_l = ok_l ? (uint32_t)row_l * LY::kRowBytes : lds_dma::kOutOfRange;
+    // DMA i covers stage rows kRowsPerDma m + j (m = I % kDmaMat, j = lane / kGran): row bits
+    // below kRowsPerDma come from j alone, and rho and swz are bit permutations, so the lane's
+    // entry and granule split into a lane part and a wave-uniform part joined by XOR
+    const int j = ln / LY::kGran;
+    const int ent_l = 4 * rho(j);                              // ds_bpermute byte address
+    const int gsw_l = ((ln % LY::kGran) ^ LY::swz(j)) << 4;    // granule byte offset
+    uint32_t voff[kDW];
+#pragma unroll
+    for (int i = 0; i < kDW; ++i) {
+      const int mrow = kRowsPerDma * ((wave * kDW + i) % kDmaMat);
+      const uint32_t rb =
+          (uint32_t)__builtin_amdgcn_ds_bpermute(ent_l ^ (4 * rho(mrow)), (int)rb_l);
+      // a row past the end stays at or above kOutOfRange, beyond the buffer's range
+      voff[i] = rb + (uint32_t)(gsw_l ^ (LY::swz(mrow) << 4));
+    }
 #pragma unroll
     for (int i = 0; i < kDW; ++i) {
       const int I = wave * kDW + i;
-      const int row = kRowsPerDma * (I % kDmaMat) + lane / LY::kGran;
-      const int e = rho(row);
-      int slot;
-      uint32_t voff = lds_dma::kOutOfRange;
-      if (c0 + e < nG)  // columns past the end read as zeros; their band test fails
-        voff = (uint32_t)col_row(slot0, rem0, e, slot) * LY::kRowBytes +
-               (uint32_t)(((lane % LY::kGran) ^ LY::swz(row)) << 4);
       lds_dma::load16(I < kDmaMat ? rs_q : rs_d,
-                      st_lds + (I / kDmaMat) * LY::kMat + (I % kDmaMat) * 1024, voff);
+                      st_lds + (I / kDmaMat) * LY::kMat + (I % kDmaMat) * 1024, voff[i]);
     }
     // waves 0, 1, 2 fetch lse, Delta, gate (lanes 0..31: the chunk's columns)
     if (wave < 3 && (wave < 2 || prm.gate)) {
-      int slot;
-      uint32_t moff = lds_dma::kOutOfRange;
-      if (lane < kChunk && c0 + lane < nG) moff = (uint32_t)col_row(slot0, rem0, lane, slot) * 4u;
+      const uint32_t moff = ln < kChunk && ok_l ? (uint32_t)row_l * 4u : lds_dma::kOutOfRange;
       lds_dma::load4(rs_m, st_lds + kMetaOff + wave * 256, moff);
     }
     if (SIGMASK && tid < kChunk) {
-      int* mi = (int*)(smem + (c & 1) * kStage + kOrigOff);
-      // the column's token, its original index (columns past the end fail the band test)
-      mi[tid] = c0 + tid < nG ? orig_of_slot(slot0 + div_small(rem0 + tid, prm.inv_g)) : -1;
+      int* mi = (int*)(smem + stage * kStage + kOrigOff);
+      // the column's original index (columns past the end fail the band test)
+      mi[tid] = ok_l ? orig_l : -1;
     }
   };
 
@@ -641,14 +669,14 @@ void bwd_dkdv_kernel(Params prm) {
   const int a_base = gran_off<D>(r32, h32);
   const int t_base0 = tr_off<D>(lane, 0, 0);
   const int t_base1 = tr_off<D>(lane, 0, 1);
-  // The band test in column space: column col_lo + x is in the band of the lane's key when its
-  // slot (col_lo + x) / G lies in [myk - R, myk + L] and the column exists (col_lo + x < nG),
-  // i.e. band_lo <= x <= band_hi.
-  const int band_lo = (myk - R) * G - col_lo;
-  const int band_hi = min(myk + L + 1, n) * G - 1 - col_lo;
+  // The band test in column space: column col_base + x is in the band of the lane's key when
+  // its slot (col_base + x) / G lies in [myk - R, myk + L] and the column exists
+  // (col_base + x < nG), i.e. band_lo <= x <= band_hi.
+  const int band_lo = (myk - R) * G - col_base;
+  const int band_hi = min(myk + L + 1, n) * G - 1 - col_base;
   // the columns inside the band of every key of the wave
-  const int wband_lo = __builtin_amdgcn_readfirstlane((wk_hi - R) * G - col_lo);
-  const int wband_hi = __builtin_amdgcn_readfirstlane(min(wk_lo + L + 1, n) * G - 1 - col_lo);
+  const int wband_lo = __builtin_amdgcn_readfirstlane((wk_hi - R) * G - col_base);
+  const int wband_hi = __builtin_amdgcn_readfirstlane(min(wk_lo + L + 1, n) * G - 1 - col_base);
   // Without a gate the stages' gate entries hold 1 (the gate DMA never writes them).
   if (!prm.gate && tid < 2 * kChunk)
     *(float*)(smem + (tid / kChunk) * kStage + kMetaOff + 128 * 4 + (tid % kChunk) * 4) = 1.0f;
@@ -657,20 +685,24 @@ void bwd_dkdv_kernel(Params prm) {
     load_sigma_seg(seg_s0);
     __syncthreads();
   }
-  dma_chunk(0);
-  for (int c = 0; c < nchunks; ++c) {
-    const int st = c & 1;
-    lds_dma::wait_vmcnt<0>();  // this wave's loads of chunk c (and, first time, the prologue's)
-    __syncthreads();           // every wave's; chunk c - 1 is scored, its stage is free
-    if (c + 1 < nchunks) {
-      const int last_slot = min(n - 1, (col_lo + (c + 2) * kChunk - 1) / G);
-      if (PERM && last_slot - seg_s0 >= kSigCap) {
-        // every read of the current segment (chunk c's loads) was before the barrier above
-        seg_s0 = (col_lo + (c + 1) * kChunk) / G;
-        load_sigma_seg(seg_s0);
-        __syncthreads();
+  dma_chunk(chunk_at(0), 0);
+  for (int i = 0; i < nchunks; ++i) {
+    const int c = chunk_at(i);
+    const int st = i & 1;
+    lds_dma::wait_vmcnt<0>();  // this wave's loads of step i (and, first time, the prologue's)
+    __syncthreads();           // every wave's; step i - 1 is scored, its stage is free
+    if (i + 1 < nchunks) {
+      if (PERM && !one_seg) {
+        // band order (c = i): move the segment when chunk c + 1 reaches past it
+        const int last_slot = min(n - 1, (col_base + (c + 2) * kChunk - 1) / G);
+        if (last_slot - seg_s0 >= kSigCap) {
+          // every read of the current segment (chunk c's loads) was before the barrier above
+          seg_s0 = (col_base + (c + 1) * kChunk) / G;
+          load_sigma_seg(seg_s0);
+          __syncthreads();
+        }
       }
-      dma_chunk(c + 1);
+      dma_chunk(chunk_at(i + 1), st ^ 1);
     }
     if (!wave_on || c < c_first || c > c_last) continue;
     const char* Qst = smem + st * kStage;
