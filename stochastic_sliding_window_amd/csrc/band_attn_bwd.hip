@@ -310,32 +310,40 @@ void bwd_dq_kernel(Params prm) {
   const uint32_t kv_range = (uint32_t)((int64_t)(n - 1) * row_stride + LY::kRowBytes);
   const lds_dma::i32x4 rs_k = lds_dma::resource(prm.k + kv_base, kv_range);
   const lds_dma::i32x4 rs_v = lds_dma::resource(prm.v + kv_base, kv_range);
-  // this wave's DMA instructions of a chunk: instruction I (wave * kDW + i) brings rows
-  // kRowsPerDma * (I % kDmaMat) + lane / kGran of matrix I / kDmaMat; lane l writes LDS slot
-  // l % kGran of its row, which holds granule (l % kGran) ^ (row % kGran) of that row
-  int dma_row[kDW];
-  uint32_t dma_goff[kDW];
-#pragma unroll
-  for (int i = 0; i < kDW; ++i) {
-    const int I = wave * kDW + i;
-    const int row = kRowsPerDma * (I % kDmaMat) + lane / LY::kGran;
-    dma_row[i] = row;
-    dma_goff[i] = (uint32_t)(((lane % LY::kGran) ^ LY::swz(row)) << 4);
-  }
   int seg_key0 = kbeg;  // first key of the current sigma segment
   auto orig_of_key = [&](int key) { return PERM ? sig_lds[key - seg_key0] : key; };
-  // keys past the sequence end read as zeros (offset out of range); the band test drops them
+  // This wave's DMA instructions of a chunk: instruction I (wave * kDW + i) brings stage rows
+  // kRowsPerDma m + j (m = I % kDmaMat, j = lane / kGran) of matrix I / kDmaMat; lane l writes
+  // LDS slot l % kGran of its row, which holds granule (l % kGran) ^ swz(row) of that row, and
+  // row r holds chunk key rho(r).  Lane l looks up the token of chunk key l % 32 once, and each
+  // instruction takes its rows' offsets from those lanes by ds_bpermute.  Row bits below
+  // kRowsPerDma come from j alone and rho and swz are bit permutations, so the lane's entry and
+  // granule split into a lane part and a wave-uniform part joined by XOR.  Keys past the
+  // sequence end read as zeros (offset out of range); the band test drops them.
   auto dma_chunk = [&](int c) {
     const int kc0 = kbeg + c * kChunk;
     const uint32_t st_lds = smem_lds + (uint32_t)((c % kDqStages) * kStage);
+    int ln = lane;  // opaque copy: the lane constants are recomputed per chunk
+    asm volatile("" : "+v"(ln));
+    const int key_l = kc0 + (ln & (kChunk - 1));
+    const uint32_t rb_l = key_l < n ? (uint32_t)orig_of_key(key_l) * row_stride
+                                    : lds_dma::kOutOfRange;
+    const int j = ln / LY::kGran;
+    const int ent_l = 4 * rho(j);
+    const int gsw_l = ((ln % LY::kGran) ^ LY::swz(j)) << 4;
+    uint32_t voff[kDW];
+#pragma unroll
+    for (int i = 0; i < kDW; ++i) {
+      const int mrow = kRowsPerDma * ((wave * kDW + i) % kDmaMat);
+      const uint32_t rb =
+          (uint32_t)__builtin_amdgcn_ds_bpermute(ent_l ^ (4 * rho(mrow)), (int)rb_l);
+      voff[i] = rb + (uint32_t)(gsw_l ^ (LY::swz(mrow) << 4));
+    }
 #pragma unroll
     for (int i = 0; i < kDW; ++i) {
       const int I = wave * kDW + i;
-      const int key = kc0 + rho(dma_row[i]);
-      const uint32_t voff = key < n ? (uint32_t)orig_of_key(key) * row_stride + dma_goff[i]
-                                    : lds_dma::kOutOfRange;
       lds_dma::load16(I < kDmaMat ? rs_k : rs_v,
-                      st_lds + (I / kDmaMat) * LY::kMat + (I % kDmaMat) * 1024, voff);
+                      st_lds + (I / kDmaMat) * LY::kMat + (I % kDmaMat) * 1024, voff[i]);
     }
   };
   auto load_sigma_seg = [&]() {
