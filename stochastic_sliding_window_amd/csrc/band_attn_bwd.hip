@@ -346,39 +346,77 @@ void bwd_dq_kernel(Params prm) {
                       st_lds + (I / kDmaMat) * LY::kMat + (I % kDmaMat) * 1024, voff[i]);
     }
   };
-  auto load_sigma_seg = [&]() {
-    for (int i = tid; i < kSigCap; i += kThreads) {
+  // sigma of the keys of the segment's chunks (keys past the end hold INT_MAX)
+  auto load_sigma_seg = [&](int nkeys) {
+    for (int i = tid; i < nkeys; i += kThreads) {
       const int key = seg_key0 + i;
       sig_lds[i] = key < n ? in_range(prm.sigma[key], n) : INT_MAX;
     }
   };
 
-  // ---- prologue: sigma of the first segment, the first chunks in flight, then the columns' Q
-  // and dy rows as B operands (k step kb holds d = 16kb + 8h32 + [0, 8)), Delta and dg
+  // ---- prologue: sigma of the first segment, two chunks in flight, the columns' O, dy and Q
+  // rows, then the third chunk
   const int seg_end0 = min(nchunks, kSegChunks);
   if constexpr (PERM) {
-    load_sigma_seg();
+    load_sigma_seg(seg_end0 * kChunk);
     __syncthreads();
   }
-  for (int c = 0; c < min(kPF, seg_end0); ++c) dma_chunk(c);
+  const int npro = min(kPF, seg_end0);
+  for (int c = 0; c < min(kPF - 1, npro); ++c) dma_chunk(c);
 
+  // The rows of the wave's 32 columns arrive whole, D / 8 lanes per row (one load instruction
+  // covers 64 / (D / 8) rows), pass through the wave's slice of ring stages 2 and 3 (not in use
+  // until the third chunk is issued) in the stage matrices' swizzled layout, and leave it as
+  // B operands: k step kb holds d = 16kb + 8h32 + [0, 8) of the lane's column.  Gathering the
+  // B operands straight from memory would touch 32 rows per load instruction.
   const int64_t rowq = ((int64_t)b * n + myorig) * prm.Hq + h;
-  const char* qrow = prm.q + rowq * LY::kRowBytes;
-  const char* drow = prm.dout + rowq * LY::kRowBytes;
-  const char* arow = prm.o + rowq * LY::kRowBytes;
   bf16x8 qf[LY::kKB], df[LY::kKB];
   float dot = 0.f;
+  {
+    constexpr int kLanesPerRow = D / 8;
+    constexpr int kRowsPerLd = 64 / kLanesPerRow;
+    constexpr int kLd = 32 / kRowsPerLd;
+    static_assert(2 * kStage >= 4 * 32 * LY::kRowBytes, "four waves' rows fit two stages");
+    const int64_t qd_batch = (int64_t)b * n * prm.Hq * LY::kRowBytes;
+    // byte offset of the lane's column row within batch row b (below 2^31, checked at the API)
+    const uint32_t my_off = (uint32_t)(((int64_t)myorig * prm.Hq + h) * LY::kRowBytes);
+    const int j = lane % kLanesPerRow;
+    u32x4 ro[kLd], rd[kLd], rq[kLd];
 #pragma unroll
-  for (int kb = 0; kb < LY::kKB; ++kb) {
-    const int off = (16 * kb + 8 * h32) * 2;
-    qf[kb] = ld_bf16x8(qrow + off);
-    const u32x4 dw = *(const u32x4*)(drow + off);
-    const u32x4 aw = *(const u32x4*)(arow + off);
-    df[kb] = __builtin_bit_cast(bf16x8, dw);
+    for (int i = 0; i < kLd; ++i) {
+      const int r = i * kRowsPerLd + lane / kLanesPerRow;
+      const int64_t off =
+          qd_batch + (uint32_t)__builtin_amdgcn_ds_bpermute(4 * r, (int)my_off) + 16 * j;
+      ro[i] = *(const u32x4*)(prm.o + off);
+      rd[i] = *(const u32x4*)(prm.dout + off);
+      rq[i] = *(const u32x4*)(prm.q + off);
+    }
+    char* reg = smem + 2 * kStage + wave * 32 * LY::kRowBytes;
+    // one matrix at a time through the slice; other lanes read what a lane wrote, so each
+    // matrix's writes complete before its reads, and its reads before the next one's writes
+    auto through_lds = [&](const u32x4* rows, u32x4* frag) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dot = __builtin_fmaf(bf_lo(dw[e]), bf_lo(aw[e]), dot);
-      dot = __builtin_fmaf(bf_hi(dw[e]), bf_hi(aw[e]), dot);
+      for (int i = 0; i < kLd; ++i)
+        *(u32x4*)(reg + gran_off<D>(i * kRowsPerLd + lane / kLanesPerRow, j)) = rows[i];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int kb = 0; kb < LY::kKB; ++kb)
+        frag[kb] = *(const u32x4*)(reg + gran_off<D>(r32, 2 * kb + h32));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    };
+    u32x4 aw[LY::kKB], dw[LY::kKB], qw[LY::kKB];
+    through_lds(ro, aw);
+    through_lds(rd, dw);
+    through_lds(rq, qw);
+#pragma unroll
+    for (int kb = 0; kb < LY::kKB; ++kb) {
+      df[kb] = __builtin_bit_cast(bf16x8, dw[kb]);
+      qf[kb] = __builtin_bit_cast(bf16x8, qw[kb]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot = __builtin_fmaf(bf_lo(dw[kb][e]), bf_lo(aw[kb][e]), dot);
+        dot = __builtin_fmaf(bf_hi(dw[kb][e]), bf_hi(aw[kb][e]), dot);
+      }
     }
   }
   dot = pair_sum(dot);
@@ -389,8 +427,12 @@ void bwd_dq_kernel(Params prm) {
     prm.delta[rowq] = delta;
     if (prm.dgate) prm.dgate[rowq] = dot;
   }
-  // every prologue load and store has completed (the loop counts only its own DMAs)
-  lds_dma::wait_vmcnt<0>();
+  // Every wave is done with stages 2 and 3, which the third chunk and the loop's first DMA
+  // take.  The Delta and dg stores need not complete first: the loop's vmcnt waits count them
+  // as well, which only makes a wait longer, and the row loads, issued after the first two
+  // chunks, have returned (in order, so those chunks have landed too).
+  __syncthreads();
+  if (kPF - 1 < npro) dma_chunk(kPF - 1);
 
   int k_off[LY::kKB];
 #pragma unroll
@@ -415,7 +457,7 @@ void bwd_dq_kernel(Params prm) {
       __syncthreads();
       seg_key0 = kbeg + seg_c0 * kChunk;
       if constexpr (PERM) {
-        load_sigma_seg();
+        load_sigma_seg((seg_end - seg_c0) * kChunk);
         __syncthreads();
       }
       for (int c = seg_c0; c < min(seg_c0 + kPF, seg_end); ++c) dma_chunk(c);
