@@ -566,8 +566,17 @@ void bwd_dkdv_kernel(Params prm) {
   static_assert(kDW >= 1 && 2 * kDmaMat == 4 * kDW, "DMA split");
   constexpr int kVOff = 2 * kStage;                      // V rows of the 128 keys
   constexpr int kSigOff = kVOff + kTile * LY::kRowBytes;
-  __shared__ __attribute__((aligned(16))) char smem[kSigOff + (PERM ? kSigCap * 4 : 0)];
+  // The last region holds either sigma (a segment of kSigCap slots) or, when the workgroup's
+  // chunks number at most kTabChunks, a table of every chunk column's row offset and (causal
+  // mode) original index.
+  constexpr int kTabChunks = 56;
+  constexpr int kTabBytes = kTabChunks * kChunk * 4 * (SIGMASK ? 2 : 1);
+  constexpr int kLastBytes = (PERM && kSigCap * 4 > kTabBytes) ? kSigCap * 4 : kTabBytes;
+  static_assert(2 * (kSigOff + kLastBytes) <= 160 * 1024, "two workgroups per CU");
+  __shared__ __attribute__((aligned(16))) char smem[kSigOff + kLastBytes];
   int* sig_lds = (int*)(smem + kSigOff);
+  uint32_t* tab_row = (uint32_t*)(smem + kSigOff);
+  int* tab_orig = (int*)(smem + kSigOff + kTabChunks * kChunk * 4);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -612,7 +621,8 @@ void bwd_dkdv_kernel(Params prm) {
   // is i modulo nchunks: workgroups of equal chunk counts that start together read each chunk
   // at the same step.  Otherwise the chunks go in band order and the segment moves along.
   const int last_slot_all = min(n - 1, (col_base + nchunks * kChunk - 1) / G);
-  const bool one_seg = !PERM || last_slot_all - col_base / G < kSigCap;
+  const bool use_tab = nchunks <= kTabChunks;
+  const bool one_seg = !PERM || use_tab || last_slot_all - col_base / G < kSigCap;
   const int a0 = col_base / kChunk;
   const int rot = one_seg ? (nchunks - a0 % nchunks) % nchunks : 0;
   auto chunk_at = [&](int i) {
@@ -658,7 +668,43 @@ void bwd_dkdv_kernel(Params prm) {
                 : wave == 1 ? (const void*)(prm.delta + qd_batch)
                             : (const void*)(prm.gate ? prm.gate + qd_batch : prm.lse + qd_batch),
       m_range);
+  // Table path: DMA instruction i of this wave covers stage rows kRowsPerDma m + j with
+  // m = kDW (wave % 2) + i and j = lane / kGran; the three parts occupy disjoint bits, and rho and
+  // swz are bit permutations, so the row's chunk entry is 16 (wave % 2) + rho(kRowsPerDma i) +
+  // rho(j) (a wave-uniform base, an immediate and a lane constant) and its granule offset a lane
+  // constant XOR an immediate.
+  static_assert(kRowsPerDma * kDW == 16 && 2 * kDW == kDmaMat, "DMA row split");
+  auto dma_chunk_tab = [&](int c, int stage) {
+    const uint32_t st_lds = smem_lds + (uint32_t)(stage * kStage);
+    uint32_t ln = lane;  // opaque copy: the lane constants are recomputed per chunk
+    asm volatile("" : "+v"(ln));
+    const int j = ln / LY::kGran;
+    const int gsw_l = ((ln % LY::kGran) ^ LY::swz(j)) << 4;
+    const uint32_t* tr = tab_row + c * kChunk + 16 * (wave & 1) + rho(j);
+    uint32_t voff[kDW];
+#pragma unroll
+    for (int i = 0; i < kDW; ++i)
+      voff[i] = tr[rho(kRowsPerDma * i)] + (uint32_t)(gsw_l ^ (LY::swz(kRowsPerDma * i) << 4));
+#pragma unroll
+    for (int i = 0; i < kDW; ++i) {
+      const int I = wave * kDW + i;
+      lds_dma::load16(I < kDmaMat ? rs_q : rs_d,
+                      st_lds + (I / kDmaMat) * LY::kMat + (I % kDmaMat) * 1024, voff[i]);
+    }
+    if (wave < 3 && (wave < 2 || prm.gate)) {
+      const uint32_t rb = tab_row[c * kChunk + (ln & (kChunk - 1))];
+      constexpr int kSh = LY::kRowBytes == 256 ? 6 : 5;  // row bytes to 4 bytes per row
+      static_assert(LY::kRowBytes == 4 << kSh, "row size");
+      const uint32_t moff =
+          ln < kChunk && rb != lds_dma::kOutOfRange ? rb >> kSh : lds_dma::kOutOfRange;
+      lds_dma::load4(rs_m, st_lds + kMetaOff + wave * 256, moff);
+    }
+  };
   auto dma_chunk = [&](int c, int stage) {
+    if (use_tab) {
+      dma_chunk_tab(c, stage);
+      return;
+    }
     const int c0 = col_base + c * kChunk;
     const int slot0 = c0 / G;  // wave-uniform
     const int rem0 = c0 - slot0 * G;
@@ -731,7 +777,20 @@ void bwd_dkdv_kernel(Params prm) {
   if (!prm.gate && tid < 2 * kChunk)
     *(float*)(smem + (tid / kChunk) * kStage + kMetaOff + 128 * 4 + (tid % kChunk) * 4) = 1.0f;
 
-  if constexpr (PERM) {
+  if (use_tab) {
+    // one entry per column of the workgroup's chunks, from sigma in global memory
+    for (int idx = tid; idx < nchunks * kChunk; idx += kThreads) {
+      const int col = col_base + idx;
+      const bool ok = col < nG;
+      const int colc = ok ? col : nG - 1;
+      const int slot = colc / G;
+      const int orig = PERM ? in_range(prm.sigma[slot], n) : slot;
+      tab_row[idx] = ok ? (uint32_t)(orig * prm.Hq + g * G + (colc - slot * G)) * LY::kRowBytes
+                        : lds_dma::kOutOfRange;
+      if constexpr (SIGMASK) tab_orig[idx] = ok ? orig : -1;
+    }
+    __syncthreads();
+  } else if constexpr (PERM) {
     load_sigma_seg(seg_s0);
     __syncthreads();
   }
@@ -774,7 +833,8 @@ void bwd_dkdv_kernel(Params prm) {
       t_off[db][1] = tb1 ^ (db << 6);
     }
     const float* mf = (const float*)(Qst + kMetaOff);  // lse [0, 64), Delta [64, ..), gate
-    const int* mi = (const int*)(Qst + kOrigOff);        // original index of each column
+    // original index of each column
+    const int* mi = use_tab ? tab_orig + c * kChunk : (const int*)(Qst + kOrigOff);
 
     // S[col][key] = <Q, K>, dP[col][key] = <dy, V>; output register i of lane half h32 holds
     // column 16(i / 8) + 8h32 + i % 8 of the chunk, for the lane's key
