@@ -311,33 +311,31 @@ void bwd_dq_kernel(Params prm) {
   const lds_dma::i32x4 rs_k = lds_dma::resource(prm.k + kv_base, kv_range);
   const lds_dma::i32x4 rs_v = lds_dma::resource(prm.v + kv_base, kv_range);
   int seg_key0 = kbeg;  // first key of the current sigma segment
-  auto orig_of_key = [&](int key) { return PERM ? sig_lds[key - seg_key0] : key; };
-  // This wave's DMA instructions of a chunk: instruction I (wave * kDW + i) brings stage rows
-  // kRowsPerDma m + j (m = I % kDmaMat, j = lane / kGran) of matrix I / kDmaMat; lane l writes
-  // LDS slot l % kGran of its row, which holds granule (l % kGran) ^ swz(row) of that row, and
-  // row r holds chunk key rho(r).  Lane l looks up the token of chunk key l % 32 once, and each
-  // instruction takes its rows' offsets from those lanes by ds_bpermute.  Row bits below
-  // kRowsPerDma come from j alone and rho and swz are bit permutations, so the lane's entry and
-  // granule split into a lane part and a wave-uniform part joined by XOR.  Keys past the
-  // sequence end read as zeros (offset out of range); the band test drops them.
+  // This wave's DMA instructions of a chunk: instruction I = wave * kDW + i brings stage rows
+  // kRowsPerDma m + j (m = I % kDmaMat = kDW (wave % 2) + i, j = lane / kGran) of matrix
+  // I / kDmaMat; lane l writes LDS slot l % kGran of its row, which holds granule
+  // (l % kGran) ^ swz(row) of that row, and row r holds chunk key rho(r).  The parts of the row
+  // occupy disjoint bits and rho and swz are bit permutations, so the key is 16 (wave % 2) +
+  // rho(kRowsPerDma i) + rho(j) (a wave-uniform base, an immediate and a lane constant) and the
+  // granule offset a lane constant XOR an immediate; each lane reads its key's token from the
+  // sigma segment itself.  Keys past the sequence end hold the token n there (or are themselves
+  // >= n), whose row lies past the buffer range and reads as zeros; the band test drops them.
+  static_assert(kRowsPerDma * kDW == 16 && 2 * kDW == kDmaMat, "DMA row split");
   auto dma_chunk = [&](int c) {
     const int kc0 = kbeg + c * kChunk;
     const uint32_t st_lds = smem_lds + (uint32_t)((c % kDqStages) * kStage);
-    int ln = lane;  // opaque copy: the lane constants are recomputed per chunk
+    uint32_t ln = lane;  // opaque copy: the lane constants are recomputed per chunk
     asm volatile("" : "+v"(ln));
-    const int key_l = kc0 + (ln & (kChunk - 1));
-    const uint32_t rb_l = key_l < n ? (uint32_t)orig_of_key(key_l) * row_stride
-                                    : lds_dma::kOutOfRange;
     const int j = ln / LY::kGran;
-    const int ent_l = 4 * rho(j);
     const int gsw_l = ((ln % LY::kGran) ^ LY::swz(j)) << 4;
+    const int key_l = kc0 + 16 * (wave & 1) + rho(j);
+    const int* sk = sig_lds + (key_l - seg_key0);
     uint32_t voff[kDW];
 #pragma unroll
     for (int i = 0; i < kDW; ++i) {
-      const int mrow = kRowsPerDma * ((wave * kDW + i) % kDmaMat);
-      const uint32_t rb =
-          (uint32_t)__builtin_amdgcn_ds_bpermute(ent_l ^ (4 * rho(mrow)), (int)rb_l);
-      voff[i] = rb + (uint32_t)(gsw_l ^ (LY::swz(mrow) << 4));
+      const int tok = PERM ? sk[rho(kRowsPerDma * i)] : key_l + rho(kRowsPerDma * i);
+      voff[i] = __umul24((uint32_t)tok, row_stride) +
+                (uint32_t)(gsw_l ^ (LY::swz(kRowsPerDma * i) << 4));
     }
 #pragma unroll
     for (int i = 0; i < kDW; ++i) {
@@ -346,11 +344,12 @@ void bwd_dq_kernel(Params prm) {
                       st_lds + (I / kDmaMat) * LY::kMat + (I % kDmaMat) * 1024, voff[i]);
     }
   };
-  // sigma of the keys of the segment's chunks (keys past the end hold INT_MAX)
+  // sigma of the keys of the segment's chunks (keys past the end hold n: no row, and every
+  // causal test fails)
   auto load_sigma_seg = [&](int nkeys) {
     for (int i = tid; i < nkeys; i += kThreads) {
       const int key = seg_key0 + i;
-      sig_lds[i] = key < n ? in_range(prm.sigma[key], n) : INT_MAX;
+      sig_lds[i] = key < n ? in_range(prm.sigma[key], n) : n;
     }
   };
 
