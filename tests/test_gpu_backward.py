@@ -130,6 +130,13 @@ LARGER = [
     ((4, 1100, 16, 16, 64, 40), "swa", True, True),
     ((2, 800, 64, 32, 128, 30), "sa", True, True),
     ((2, 800, 64, 32, 128, 30), "swa", False, False),
+    # the dK/dV kernel keeps a table of its chunk columns' rows when a workgroup has at most 56
+    # chunks and reads sigma segments otherwise; at n 1600, G 4 the workgroups have up to 56
+    # chunks (w 161), 56 and 64 in one launch (w 190), and 57 and more past the table (w 194)
+    ((1, 1600, 8, 2, 128, 161), "sa", True, True),
+    ((1, 1600, 8, 2, 128, 190), "sa", True, False),
+    ((1, 1600, 8, 2, 128, 194), "sa", False, True),
+    ((1, 1600, 8, 2, 128, 194), "swa", False, False),
 ]
 
 
