@@ -653,8 +653,10 @@ void bwd_dkdv_kernel(Params prm) {
   auto orig_of_slot = [&](int slot) { return PERM ? sig_lds[slot - seg_s0] : slot; };
 
   // ---- chunk staging: direct buffer-to-LDS loads of the chunk's Q and dy rows (MFMA row order,
-  // granules swizzled by row) and of its columns' lse, Delta and gate; the original index of each
-  // column is written by the first 32 threads (causal mode).  One chunk is in flight while the
+  // granules swizzled by row) and of its columns' lse, Delta and gate.  The columns' rows and, in
+  // causal mode, original indices come from the row table when there is one; otherwise each
+  // chunk's rows are looked up through the sigma segment as the chunk is issued, and the first 32
+  // threads write its original indices into the stage.  One chunk is in flight while the
   // previous one is scored (two stages: the V rows of the tile take the rest of the LDS).
   const uint32_t smem_lds = lds_dma::lds_addr(smem);
   const int64_t qd_batch = (int64_t)b * n * prm.Hq;
