@@ -137,6 +137,7 @@ LARGER = [
     ((1, 1600, 8, 2, 128, 190), "sa", True, False),
     ((1, 1600, 8, 2, 128, 194), "sa", False, True),
     ((1, 1600, 8, 2, 128, 194), "swa", False, False),
+    ((1, 1600, 8, 2, 64, 194), "sa", True, True),    # the same at d 64
 ]
 
 

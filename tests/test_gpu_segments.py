@@ -120,20 +120,22 @@ def _np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("causal,B", [(True, 1), (False, 1), (True, 8)])
-def test_sa_backward_band_over_two_sigma_segments(causal, B):
+@pytest.mark.parametrize("causal,B,d", [(True, 1, 128), (False, 1, 128), (True, 8, 128),
+                                         (True, 1, 64)])
+def test_sa_backward_band_over_two_sigma_segments(causal, B, d):
     """dq of sampled query rows and (causal) dk, dv of sampled key rows of SA with a gate, at a
     band over two sigma segments of the dQ (2231 keys per tile) and dK/dV (128 + 2198 query
-    slots per tile) kernels; B = 8 also checks batch rows past the first."""
-    n, Hq, Hkv, d, w = 4096, 8, 2, 128, W_LONG
-    seed = 8300 + (1 if causal else 0)
+    slots per tile) kernels; B = 8 also checks batch rows past the first, d = 64 the other
+    head size's build of both kernels."""
+    n, Hq, Hkv, w = 4096, 8, 2, W_LONG
+    seed = 8300 + (1 if causal else 0) + (2 if d == 64 else 0)
     q, k, v = synth.qkv(seed, B, n, Hq, Hkv, d, "bf16")
     g = synth.gates(seed, B, n, Hq)
     dy = synth.upstream_grad(seed, B, n, Hq, d, "bf16")
     sig_dev, sig = _sigma(seed + 1, n)
     qd, kd, vd, dyd = q.to(DEV), k.to(DEV), v.to(DEV), dy.to(DEV)
     gate = g[0].contiguous().to(DEV)
-    _say(f"segments sa backward causal={causal} n={n} w={w}")
+    _say(f"segments sa backward causal={causal} B={B} d={d} n={n} w={w}")
     out, lse = ssw.sa_forward_lse(qd, kd, vd, sig_dev, w, causal)
     dq, dk, dv, dg = ssw.sa_backward(qd, kd, vd, sig_dev, w, causal, out, lse, dyd, gate=gate)
     torch.cuda.synchronize()
