@@ -549,9 +549,9 @@ void bwd_dq_kernel(Params prm) {
 // ------------------------------------------------------------------------------------------------
 // The V rows of the workgroup's keys sit in LDS rather than in registers: the K operand and the
 // two accumulators already take 160 registers per lane at d = 128, and two waves per SIMD need
-// the total to stay within 256.  At d = 64 the kernel fits 168 registers (one value spilled in
-// the loop), which gives three waves per SIMD and three workgroups per CU: the 360M-shaped
-// gated backward took 444 us against 470-474 us at two.
+// the total to stay within 256.  At d = 64 the kernel fits 168 registers (in causal mode one
+// value goes to scratch and back per chunk), which gives three waves per SIMD and three
+// workgroups per CU: the 360M-shaped gated backward took 444 us against 470-474 us at two.
 template <int D, bool PERM, bool SIGMASK>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
