@@ -618,10 +618,11 @@ void bwd_dkdv_kernel(Params prm) {
   const int c_first = (max(0, wk_lo - R) * G - col_base) / kChunk;
   const int c_last = (min(n - 1, wk_hi + L) * G + G - 1 - col_base) / kChunk;
   // Visiting order.  About three neighbouring workgroups read each chunk, and in band order they
-  // would reach it many chunks apart, after the L2 has cycled.  So, when the sigma of every slot
-  // the chunks touch fits one LDS segment, step i takes the chunk whose index on the common grid
-  // is i modulo nchunks: workgroups of equal chunk counts that start together read each chunk
-  // at the same step.  Otherwise the chunks go in band order and the segment moves along.
+  // would reach it many chunks apart, after the L2 has cycled.  So, when every chunk's rows are
+  // known from the start (the row table, or the sigma of every slot the chunks touch in one LDS
+  // segment), step i takes the chunk whose index on the common grid is i modulo nchunks:
+  // workgroups of equal chunk counts that start together read each chunk at the same step.
+  // Otherwise the chunks go in band order and the segment moves along.
   const int last_slot_all = min(n - 1, (col_base + nchunks * kChunk - 1) / G);
   const bool use_tab = nchunks <= kTabChunks;
   const bool one_seg = !PERM || use_tab || last_slot_all - col_base / G < kSigCap;
